@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the QLoRA linear layer.
+
+This module draws random numbers and rounds them to the storage dtype; it holds
+none of the method's arithmetic. Both the tests (for the HIP path and for the
+CPU oracle) and the benchmark take their inputs from here, so the two sides see
+identical bytes.
+
+Recipe (shapes from the LLaMA/Qwen-style projections the workloads name):
+  * RNG: numpy.random.default_rng([seed, config, projection, tensor]) with
+    tensor ids W=0, A=1, B=2, x=3, dY=4;
+  * W  ~ N(0, 0.02^2) float32 (bf16-rounded where the workload loads bf16 weights);
+  * A, B ~ N(0, 0.02^2) rounded to bf16;
+  * x, dY ~ N(0, 1) rounded to bf16.
+Rounding to bf16 uses torch's own float32 -> bfloat16 conversion.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+T_W, T_A, T_B, T_X, T_DY = 0, 1, 2, 3, 4
+
+
+@dataclass(frozen=True)
+class Projection:
+    name: str
+    d_out: int
+    d_in: int
+    r: int           # LoRA rank, 0 = frozen projection without adapter
+    alpha: float
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    description: str
+    projections: tuple
+    tokens: tuple     # token counts T exercised
+    backward: bool
+    weight_dtype: str  # "f32" or "bf16"
+    layers: int = 1
+
+
+WORKLOADS = {
+    "c1": Workload("c1", "single linear 1024x1024, LoRA r=8 alpha=16, 16 tokens, fwd+bwd",
+                   (Projection("linear", 1024, 1024, 8, 16.0),), (16,), True, "f32"),
+    "c2": Workload("c2", "LLaMA-7B projections 4096x4096 and 11008x4096, LoRA r=64 alpha=16, "
+                   "1/4/16 tokens, forward",
+                   (Projection("q_proj", 4096, 4096, 64, 16.0),
+                    Projection("up_proj", 11008, 4096, 64, 16.0)), (1, 4, 16), False, "f32"),
+    "c3": Workload("c3", "13B projections 5120x5120 and 13824x5120, LoRA r=64 alpha=16, "
+                   "4096 tokens (8x512), fwd+bwd",
+                   (Projection("q_proj", 5120, 5120, 64, 16.0),
+                    Projection("up_proj", 13824, 5120, 64, 16.0)), (4096,), True, "f32"),
+    "c4": Workload("c4", "65B decoder layer, hidden 8192, MLP 22016, LoRA r=64 alpha=16 on all "
+                   "projections, 4096 tokens, fwd+bwd",
+                   (Projection("q_proj", 8192, 8192, 64, 16.0),
+                    Projection("k_proj", 8192, 8192, 64, 16.0),
+                    Projection("v_proj", 8192, 8192, 64, 16.0),
+                    Projection("o_proj", 8192, 8192, 64, 16.0),
+                    Projection("gate_proj", 22016, 8192, 64, 16.0),
+                    Projection("up_proj", 22016, 8192, 64, 16.0),
+                    Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
+    # 14B-style stack: k/v are 1024x5120 (8 KV heads x 128); LoRA r=8 on q and v only.
+    "c5": Workload("c5", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 alpha=16 "
+                   "on q/v, 2048 tokens, fwd+bwd",
+                   (Projection("q_proj", 5120, 5120, 8, 16.0),
+                    Projection("k_proj", 1024, 5120, 0, 16.0),
+                    Projection("v_proj", 1024, 5120, 8, 16.0),
+                    Projection("o_proj", 5120, 5120, 0, 16.0),
+                    Projection("gate_proj", 17408, 5120, 0, 16.0),
+                    Projection("up_proj", 17408, 5120, 0, 16.0),
+                    Projection("down_proj", 5120, 17408, 0, 16.0)), (2048,), True, "bf16", layers=40),
+}
+CONFIG_INDEX = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+
+
+def rng(config: int, projection: int, tensor: int, seed: int = 0) -> np.random.Generator:
+    return np.random.default_rng([seed, config, projection, tensor])
+
+
+def to_bf16(a: np.ndarray):
+    """Round float32 -> bf16 with torch; returns (values as float32, uint16 bit patterns)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.float().numpy(), bits
+
+
+def normal(g: np.random.Generator, shape, std: float) -> np.ndarray:
+    out = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def weight(config: int, projection: int, d_out: int, d_in: int, dtype: str = "f32", seed: int = 0):
+    """W ~ N(0, 0.02^2), float32; bf16-rounded (still returned as float32 values) when dtype == 'bf16'."""
+    w = normal(rng(config, projection, T_W, seed), (d_out, d_in), 0.02)
+    if dtype == "bf16":
+        w, _ = to_bf16(w)
+    return w
+
+
+def adapters(config: int, projection: int, d_out: int, d_in: int, r: int, seed: int = 0):
+    """A [r, d_in], B [d_out, r] ~ N(0, 0.02^2) in bf16: ((A_val, A_bits), (B_val, B_bits))."""
+    A = to_bf16(normal(rng(config, projection, T_A, seed), (r, d_in), 0.02))
+    B = to_bf16(normal(rng(config, projection, T_B, seed), (d_out, r), 0.02))
+    return A, B
+
+
+def tokens(config: int, projection: int, T: int, d_in: int, seed: int = 0):
+    """x [T, d_in] ~ N(0, 1) in bf16: (values, bits)."""
+    return to_bf16(normal(rng(config, projection, T_X, seed), (T, d_in), 1.0))
+
+
+def upstream_grad(config: int, projection: int, T: int, d_out: int, seed: int = 0):
+    """dY [T, d_out] ~ N(0, 1) in bf16: (values, bits)."""
+    return to_bf16(normal(rng(config, projection, T_DY, seed), (T, d_out), 1.0))

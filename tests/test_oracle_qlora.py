@@ -1,0 +1,154 @@
+"""Pins for the oracle's QLoRA forward and backward (CPU only).
+
+  * brute force on tiny, non-square inputs: the pages' column-vector equation
+    h = W_hat x + (alpha/r) B A x evaluated token by token with Python loops;
+  * special cases the pages state: B = 0 gives exactly the base model's output
+    (48GB, "LoRA Freezes the Original Weights"); a zero weight quantizes to all
+    zero codes and leaves only the LoRA term;
+  * linearity in x;
+  * central finite differences of L = <dY, h> in A, B and x (h is linear in
+    each, so agreement is to rounding);
+  * float64 torch.autograd over the same restored weight, with W a constant;
+  * no gradient into W.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_finetuning_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def _setup(d_out, d_in, r, T, seed=0, wscale=0.02):
+    rs = np.random.default_rng(seed)
+    W = (rs.standard_normal((d_out, d_in)) * wscale).astype(np.float32)
+    codes, q2, S = oracle.quantize(W)
+    _, Wh = oracle.dequantize(codes, q2, S, d_out, d_in)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    x = bf(rs.standard_normal((T, d_in)))
+    A = bf(rs.standard_normal((r, d_in)) * 0.02)
+    B = bf(rs.standard_normal((d_out, r)) * 0.02)
+    dY = bf(rs.standard_normal((T, d_out)))
+    return Wh, x, A, B, dY
+
+
+def test_forward_bruteforce_column_vector_form():
+    d_out, d_in, r, T, alpha = 3, 64, 2, 2, 16.0
+    Wh, x, A, B, _ = _setup(d_out, d_in, r, T, seed=4)
+    h, u = oracle.lora_forward(Wh, x, A, B, alpha, r)
+    s = float(np.float32(alpha) / np.float32(r))
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        Ax = [sum(float(A[j][i]) * xt[i] for i in range(d_in)) for j in range(r)]
+        for o in range(d_out):
+            base = sum(float(Wh[o][i]) * xt[i] for i in range(d_in))
+            lora = sum(float(B[o][j]) * Ax[j] for j in range(r))
+            assert h[t, o] == pytest.approx(base + s * lora, rel=1e-12, abs=1e-14)
+        for j in range(r):
+            assert u[t, j] == pytest.approx(Ax[j], rel=1e-12, abs=1e-14)
+
+
+def test_zero_B_gives_base_model_output_exactly():
+    Wh, x, A, B, _ = _setup(96, 128, 4, 5)
+    h0, _ = oracle.lora_forward(Wh, x, A, np.zeros_like(B), 16.0, 4)
+    hb, _ = oracle.lora_forward(Wh, x, None, None, 16.0, 0)
+    assert np.array_equal(h0 + 0.0, hb + 0.0)
+
+
+def test_zero_weight_leaves_only_lora_term():
+    W = np.zeros((64, 128), dtype=np.float32)
+    codes, q2, S = oracle.quantize(W)
+    assert np.all(codes == 0x77) and np.all(q2 == 0) and np.all(S == 0)
+    _, Wh = oracle.dequantize(codes, q2, S, 64, 128)
+    assert np.all(Wh == 0)
+    _, x, A, B, _ = _setup(64, 128, 4, 3)
+    h, u = oracle.lora_forward(Wh, x, A, B, 16.0, 4)
+    s = float(np.float32(16.0) / np.float32(4))
+    ref = s * (x.astype(np.float64) @ A.T.astype(np.float64)) @ B.T.astype(np.float64)
+    assert np.allclose(h, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_forward_linear_in_x():
+    Wh, x, A, B, _ = _setup(64, 128, 4, 6)
+    x1, x2 = x[:3], x[3:]
+    h1, _ = oracle.lora_forward(Wh, x1, A, B, 16.0, 4)
+    h2, _ = oracle.lora_forward(Wh, x2, A, B, 16.0, 4)
+    h12, _ = oracle.lora_forward(Wh, x1 + x2, A, B, 16.0, 4)
+    assert np.allclose(h12, h1 + h2, rtol=1e-12, atol=1e-12)
+
+
+def _loss(Wh, x, A, B, dY, alpha, r):
+    h, _ = oracle.lora_forward(Wh, x, A, B, alpha, r)
+    return float(np.sum(h * dY.astype(np.float64)))
+
+
+@pytest.mark.parametrize("which", ["A", "B", "x"])
+def test_backward_central_finite_differences(which):
+    d_out, d_in, r, T, alpha = 128, 128, 4, 3, 16.0
+    Wh, x, A, B, dY = _setup(d_out, d_in, r, T, seed=2)
+    dX, dA, dB = oracle.lora_backward(Wh, x, dY, A, B, alpha, r)
+    A, B, x = A.astype(np.float64), B.astype(np.float64), x.astype(np.float64)
+    target = {"A": (A, dA), "B": (B, dB), "x": (x, dX)}[which]
+    arr, grad = target
+    rs = np.random.default_rng(99)
+    idx = [tuple(rs.integers(0, n) for n in arr.shape) for _ in range(25)]
+    eps = 1e-3
+    for ix in idx:
+        keep = arr[ix]
+        arr[ix] = keep + eps
+        lp = _loss(Wh, x, A, B, dY, alpha, r)
+        arr[ix] = keep - eps
+        lm = _loss(Wh, x, A, B, dY, alpha, r)
+        arr[ix] = keep
+        fd = (lp - lm) / (2 * eps)
+        assert fd == pytest.approx(grad[ix], rel=1e-7, abs=1e-9)
+
+
+def test_backward_matches_float64_autograd_and_no_weight_gradient():
+    d_out, d_in, r, T, alpha = 96, 192, 8, 5, 16.0
+    Wh, x, A, B, dY = _setup(d_out, d_in, r, T, seed=8)
+    dX, dA, dB = oracle.lora_backward(Wh, x, dY, A, B, alpha, r)
+    Wt = torch.tensor(Wh, dtype=torch.float64)                   # frozen: requires_grad False
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    At = torch.tensor(A, dtype=torch.float64, requires_grad=True)
+    Bt = torch.tensor(B, dtype=torch.float64, requires_grad=True)
+    s = float(np.float32(alpha) / np.float32(r))
+    h = torch.nn.functional.linear(xt, Wt) + s * torch.nn.functional.linear(
+        torch.nn.functional.linear(xt, At), Bt)
+    h.backward(torch.tensor(dY, dtype=torch.float64))
+    assert Wt.grad is None
+    assert np.allclose(dX, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dA, At.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dB, Bt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rank_zero_backward_is_base_only():
+    Wh, x, A, B, dY = _setup(64, 128, 4, 3)
+    dX, dA, dB = oracle.lora_backward(Wh, x, dY, None, None, 16.0, 0)
+    assert dA is None and dB is None
+    assert np.allclose(dX, dY.astype(np.float64) @ Wh.astype(np.float64))
+
+
+def test_lora_parameter_counts_from_pages():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    # 48GB page: d = 4096, r = 8 -> 2 d r = 65,536 numbers, ~0.4% of d^2 (~16.8 M)
+    d, r = 4096, 8
+    assert 2 * d * r == g["lora_params_d4096_r8"]["value"]
+    assert abs(d * d - g["dense_params_d4096"]["value"]) / g["dense_params_d4096"]["value"] < 0.01
+    assert round(2 * d * r / (d * d), 3) == g["lora_fraction_d4096_r8"]["value"]
+    # GPU-fit page: Qwen3-14B with LoRA r=8 on q_proj, v_proj has 5.24 M trainable parameters;
+    # the 14B-style stack workload (40 layers, q 5120x5120, v 1024x5120) reproduces it.
+    wl = synth.WORKLOADS["c5"]
+    n = 0
+    for p in wl.projections:
+        if p.r:
+            n += p.r * (p.d_in + p.d_out)
+    n *= wl.layers
+    assert round(n / 1e6, 2) == g["qwen3_14b_lora_q_v_r8_params"]["value"] / 1e6
