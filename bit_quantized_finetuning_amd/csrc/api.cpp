@@ -1,0 +1,294 @@
+// C ABI of the QLoRA frozen-NF4 linear layer: validation, workspace layout and
+// kernel dispatch. Every entry point validates all arguments on the host before
+// enqueuing anything; the library allocates no memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/qlora.h"
+#include "kernels.h"
+
+using namespace qlora;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// NF4 codebook: normal quantiles with an exact zero, dense near zero ("48GB GPU
+// Fine-Tuning a 65B Model", section "Quantization Keeps the Patterns..."):
+// 8 positive levels Phi^-1(1/2 + (p - 1/2) j/8), j = 1..8, 7 negative levels
+// -Phi^-1(1/2 + (p - 1/2) j/7), j = 1..7, and 0, with p = ((1-1/30)+(1-1/32))/2,
+// divided by Phi^-1(p) so the extremes are exactly +-1, rounded to float32.
+// The quantile is found by bisection on Phi(x) = erfc(-x/sqrt(2))/2 in double.
+// ---------------------------------------------------------------------------
+double normal_quantile(double p) {
+  double lo = -12.0, hi = 12.0;
+  for (int it = 0; it < 400; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+struct Tables {
+  Nf4Consts c;
+  Tables() {
+    const double p = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+    std::vector<double> v;
+    for (int j = 1; j <= 8; ++j) v.push_back(normal_quantile(0.5 + (p - 0.5) * j / 8.0));
+    for (int j = 1; j <= 7; ++j) v.push_back(-normal_quantile(0.5 + (p - 0.5) * j / 7.0));
+    v.push_back(0.0);
+    std::sort(v.begin(), v.end());
+    const double top = normal_quantile(p);
+    for (int j = 0; j < 16; ++j) c.code[j] = (float)(v[j] / top);
+    // Decision thresholds: smallest float32 strictly above each midpoint of two
+    // adjacent levels, so (x >= thr[j]) <=> (x > midpoint) for float32 x and the
+    // nearest level wins with ties going to the lower index.
+    for (int j = 0; j < 15; ++j) {
+      const double m = 0.5 * ((double)c.code[j] + (double)c.code[j + 1]);
+      float f = (float)m;
+      if ((double)f <= m) f = std::nextafter(f, INFINITY);
+      c.thr[j] = f;
+    }
+    c.pad_ = 0.f;
+  }
+};
+
+const Nf4Consts &consts() {
+  static const Tables t;
+  return t.c;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int validate_weight(const qlora_nf4_weight *W) {
+  if (!W || !W->codes || !W->qscale || !W->smax) return QLORA_ERR_NULL;
+  if (W->d_out < 1 || W->d_in < QLORA_BLOCK || W->d_in % QLORA_BLOCK != 0 || W->d_out % 16 != 0)
+    return QLORA_ERR_SHAPE;
+  if (W->d_out > (int64_t)1 << 31 || W->d_in > (int64_t)1 << 31) return QLORA_ERR_SHAPE;
+  if (!aligned16(W->codes) || !aligned16(W->qscale) || !aligned16(W->smax)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int rank_pad(int r) { return r > 0 ? (int)ceil_div(r, 16) * 16 : 0; }
+
+int lora_small_ksplit(int64_t T, int64_t K) {
+  if (T > 64) return 1;
+  int64_t ks = ceil_div(K, 32) / 8;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(ks, 64));
+}
+
+// Workspace regions (byte offsets). The counter region is fixed (kMaxCounters
+// u32 at offset 0, independent of the shapes) so that a workspace reused across
+// calls of different sizes always finds its counters zero: every kernel that
+// counts arriving workgroups resets its counters before it exits, and the calls
+// of one stream run one kernel at a time.
+struct Layout {
+  size_t sx, u, v, bt, partial, total;
+};
+
+Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
+  Layout L{};
+  const int rp = rank_pad(r);
+  const int64_t T16 = std::max<int64_t>(16, ceil_div(T, 16) * 16);
+  size_t off = align256((size_t)kMaxCounters * sizeof(uint32_t));
+  L.sx = off;
+  off = align256(off + (size_t)T16 * rp * 2);
+  L.u = off;
+  off = align256(off + (size_t)T * r * 4);
+  L.v = off;
+  off = align256(off + (size_t)T * r * 4);
+  L.bt = off;
+  off = align256(off + (size_t)r * d_out * 2);
+  size_t pf = 0;
+  if (T <= 16) pf = std::max(pf, (size_t)ceil_div(d_out, 64) * gemv_ksplit(d_out, d_in) * 1024);
+  if (r > 0) {
+    pf = std::max(pf, (size_t)ceil_div(T, 16) * lora_small_ksplit(T, std::max(d_in, d_out)) * 16 * rp);
+    pf = std::max(pf, lora_grad_partial_floats(r, d_in, T));
+    pf = std::max(pf, lora_grad_partial_floats(d_out, r, T));
+  }
+  L.partial = off;
+  off = align256(off + pf * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<uint8_t *>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+void qlora_nf4_codebook(float out[16]) {
+  if (out) std::memcpy(out, consts().code, 16 * sizeof(float));
+}
+
+void qlora_nf4_thresholds(float out[15]) {
+  if (out) std::memcpy(out, consts().thr, 15 * sizeof(float));
+}
+
+const char *qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "invalid shape (need d_in % 64 == 0, d_out % 16 == 0, T >= 1, 0 <= r <= 256, r % 8 == 0)";
+    case QLORA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_DTYPE: return "unknown dtype";
+    case QLORA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t qlora_storage_bytes(int64_t d_out, int64_t d_in) {
+  if (d_out < 1 || d_in < 1) return 0;
+  const int64_t n = d_out * d_in, nb = n / QLORA_BLOCK;
+  return (size_t)(n / 2 + nb + 4 * ceil_div(nb, QLORA_GROUP));
+}
+
+size_t qlora_workspace_bytes(int64_t d_out, int64_t d_in, int64_t T, int32_t r) {
+  if (d_out < 1 || d_in < 1 || T < 1 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  return layout(d_out, d_in, T, r).total;
+}
+
+int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint32_t *flags, hipStream_t stream) {
+  if (!W) return QLORA_ERR_NULL;
+  int s = validate_weight(out);
+  if (s) return s;
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (!aligned16(W) || (flags && (reinterpret_cast<uintptr_t>(flags) & 3u))) return QLORA_ERR_ALIGN;
+  return hip_status(launch_quantize(W, w_dtype == QLORA_BF16, out->d_out, out->d_in, out->codes, out->qscale,
+                                    out->smax, flags, consts(), stream));
+}
+
+int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStream_t stream) {
+  int s = validate_weight(W);
+  if (s) return s;
+  if (!out) return QLORA_ERR_NULL;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (!aligned16(out)) return QLORA_ERR_ALIGN;
+  return hip_status(launch_dequantize(W->codes, W->qscale, W->smax, W->d_out, W->d_in, out_dtype == QLORA_BF16, out,
+                                      consts(), stream));
+}
+
+int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
+                  int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  int s = validate_weight(W);
+  if (s) return s;
+  if (!x || !h) return QLORA_ERR_NULL;
+  if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (T > (int64_t)1 << 24) return QLORA_ERR_SHAPE;
+  if (!A && !B) r = 0;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(h) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+      (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  const int64_t d_out = W->d_out, d_in = W->d_in;
+  const Layout L = layout(d_out, d_in, T, r);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if (!ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+
+  const Nf4Consts &c = consts();
+  const int rp = rank_pad(r);
+  const float sc = r > 0 ? alpha / (float)r : 0.f;
+  uint16_t *su = at<uint16_t>(ws, L.sx);
+  float *partial = at<float>(ws, L.partial);
+  hipError_t e = hipSuccess;
+  if (r > 0) {
+    const int ks = lora_small_ksplit(T, d_in);
+    e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks,
+                          stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (T <= 16)
+    e = launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
+                        at<uint32_t>(ws, 0), gemv_ksplit(d_out, d_in), c, stream);
+  else
+    e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, c, stream);
+  return hip_status(e);
+}
+
+int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t *dY, int64_t T, const uint16_t *A,
+                   const uint16_t *B, int32_t r, float alpha, const float *u_saved, uint16_t *dX, float *dA,
+                   float *dB, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int s = validate_weight(W);
+  if (s) return s;
+  if (!dY) return QLORA_ERR_NULL;
+  if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (T > (int64_t)1 << 24) return QLORA_ERR_SHAPE;
+  if (!A && !B) r = 0;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (r == 0 && (dA || dB)) return QLORA_ERR_SHAPE;
+  if (dA && !x) return QLORA_ERR_NULL;
+  if (dB && !u_saved && !x) return QLORA_ERR_NULL;
+  if (!aligned16(dY) || (x && !aligned16(x)) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+      (u_saved && !aligned16(u_saved)) || (dX && !aligned16(dX)) || (dA && !aligned16(dA)) ||
+      (dB && !aligned16(dB)))
+    return QLORA_ERR_ALIGN;
+  const int64_t d_out = W->d_out, d_in = W->d_in;
+  const Layout L = layout(d_out, d_in, T, r);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if (!ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (!dX && !dA && !dB) return QLORA_OK;
+
+  const Nf4Consts &c = consts();
+  const int rp = rank_pad(r);
+  const float sc = r > 0 ? alpha / (float)r : 0.f;
+  uint16_t *sv = at<uint16_t>(ws, L.sx);
+  float *v = at<float>(ws, L.v);
+  float *partial = at<float>(ws, L.partial);
+  uint32_t *cnt_small = at<uint32_t>(ws, 0);
+  hipError_t e = hipSuccess;
+  const float *u = u_saved;
+  if (r > 0) {
+    uint16_t *bt = at<uint16_t>(ws, L.bt);
+    e = launch_transpose_bf16(B, d_out, r, bt, stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+    e = launch_lora_small(dY, bt, T, d_out, r, sc, v, sv, rp, partial, cnt_small, lora_small_ksplit(T, d_out),
+                          stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dX) {
+    e = launch_gemm_dx(W->codes, W->qscale, W->smax, d_out, d_in, dY, T, sv, rp, A, r, dX, c, stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dA) {
+    e = launch_lora_grad(v, true, r, x, false, d_in, T, sc, dA, partial, at<uint32_t>(ws, 0),
+                         lora_grad_ksplit(r, d_in, T), stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dB) {
+    if (!u) {
+      float *uw = at<float>(ws, L.u);
+      e = launch_lora_small(x, A, T, d_in, r, 1.f, uw, nullptr, rp, partial, cnt_small, lora_small_ksplit(T, d_in),
+                            stream);
+      if (e != hipSuccess) return QLORA_ERR_HIP;
+      u = uw;
+    }
+    e = launch_lora_grad(dY, false, d_out, u, true, r, T, sc, dB, partial, at<uint32_t>(ws, 0),
+                         lora_grad_ksplit(d_out, r, T), stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal host-side launchers of the gfx950 kernels. Called only by api.cpp after
+// argument validation; every launcher enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qlora {
+
+// quantize.hip
+hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d_in, uint8_t *codes,
+                           uint8_t *qscale, float *smax, uint32_t *flags, const Nf4Consts &c,
+                           hipStream_t st);
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const float *smax,
+                             int64_t d_out, int64_t d_in, bool bf16_out, void *out, const Nf4Consts &c,
+                             hipStream_t st);
+
+// lora_small.hip: out[T, r] = P[T, K] . Q^T with Q given as [r, K] (K contiguous).
+// Writes out_f32 (nullable) and out_bf16 = bf16(scale * out) with row pitch r_pad
+// (zero-filled up to r_pad, a multiple of 16). Uses `partial` (ksplit*16*r_pad f32
+// per 16-token tile) and `counters` (one per 16-token tile) when ksplit > 1.
+hipError_t launch_lora_small(const uint16_t *P, const uint16_t *Q, int64_t T, int64_t K, int r,
+                             float scale, float *out_f32, uint16_t *out_bf16, int r_pad, float *partial,
+                             uint32_t *counters, int ksplit, hipStream_t st);
+// B [rows, cols] bf16 -> Bt [cols, rows] bf16
+hipError_t launch_transpose_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst,
+                                 hipStream_t st);
+
+// gemv.hip: T <= 16. h[T, d_out] = x W_hat^T + su B^T (su = bf16(s*u) [16, r_pad], B [d_out, r]).
+hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
+                           int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *su, int r_pad,
+                           const uint16_t *B, int r, uint16_t *h, float *partial, uint32_t *counters,
+                           int ksplit, const Nf4Consts &c, hipStream_t st);
+int gemv_ksplit(int64_t d_out, int64_t d_in);
+
+// gemm.hip: T > 16.
+hipError_t launch_gemm_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
+                           int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *su, int r_pad,
+                           const uint16_t *B, int r, uint16_t *h, const Nf4Consts &c, hipStream_t st);
+// dX[T, d_in] = dY W_hat + sv A (sv = bf16(s*v) [T, r_pad], A [r, d_in]).
+hipError_t launch_gemm_dx(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
+                          int64_t d_in, const uint16_t *dY, int64_t T, const uint16_t *sv, int r_pad,
+                          const uint16_t *A, int r, uint16_t *dX, const Nf4Consts &c, hipStream_t st);
+
+// lora_grad.hip: C[M, N] = scale * sum_t P[t, m] Q[t, n] over t < T.
+// P and Q are each bf16 or f32 (an f32 operand is split into two bf16 terms).
+hipError_t launch_lora_grad(const void *P, bool P_f32, int64_t M, const void *Q, bool Q_f32, int64_t N,
+                            int64_t T, float scale, float *C, float *partial, uint32_t *counters,
+                            int ksplit, hipStream_t st);
+int lora_grad_ksplit(int64_t M, int64_t N, int64_t T);
+size_t lora_grad_partial_floats(int64_t M, int64_t N, int64_t T);
+int lora_grad_tiles(int64_t M, int64_t N);
+
+}  // namespace qlora

@@ -1,0 +1,229 @@
+"""Thin Python binding over libqlora.so (ctypes).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device memory and the current HIP stream; the library itself
+allocates nothing. If the library is missing this module raises at import --
+there is no fallback path.
+
+Function names follow the C ABI in include/qlora.h:
+    qlora_quantize, qlora_dequantize, qlora_forward, qlora_backward,
+    qlora_storage_bytes, qlora_workspace_bytes, qlora_nf4_codebook,
+    qlora_nf4_thresholds, qlora_status_string
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+BLOCK = 64
+GROUP = 256
+MAX_RANK = 256
+
+F32, BF16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m bit_quantized_finetuning_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _Nf4Weight(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("qscale", ctypes.c_void_p), ("smax", ctypes.c_void_p)]
+
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_W = ctypes.POINTER(_Nf4Weight)
+
+_lib.qlora_quantize.argtypes = [_vp, ctypes.c_int, _W, _vp, _vp]
+_lib.qlora_quantize.restype = ctypes.c_int
+_lib.qlora_dequantize.argtypes = [_W, ctypes.c_int, _vp, _vp]
+_lib.qlora_dequantize.restype = ctypes.c_int
+_lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+_lib.qlora_forward.restype = ctypes.c_int
+_lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.qlora_backward.restype = ctypes.c_int
+_lib.qlora_storage_bytes.argtypes = [_i64, _i64]
+_lib.qlora_storage_bytes.restype = _sz
+_lib.qlora_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
+_lib.qlora_workspace_bytes.restype = _sz
+_lib.qlora_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+_lib.qlora_nf4_codebook.restype = None
+_lib.qlora_nf4_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
+_lib.qlora_nf4_thresholds.restype = None
+_lib.qlora_status_string.argtypes = [ctypes.c_int]
+_lib.qlora_status_string.restype = ctypes.c_char_p
+
+lib = _lib  # raw handle, for tests of the C ABI itself
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.qlora_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QloraError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# host helpers (no GPU needed)
+# ---------------------------------------------------------------------------
+
+def qlora_nf4_codebook():
+    buf = (ctypes.c_float * 16)()
+    _lib.qlora_nf4_codebook(buf)
+    return list(buf)
+
+
+def qlora_nf4_thresholds():
+    buf = (ctypes.c_float * 15)()
+    _lib.qlora_nf4_thresholds(buf)
+    return list(buf)
+
+
+def qlora_storage_bytes(d_out: int, d_in: int) -> int:
+    return int(_lib.qlora_storage_bytes(d_out, d_in))
+
+
+def qlora_workspace_bytes(d_out: int, d_in: int, T: int, r: int) -> int:
+    return int(_lib.qlora_workspace_bytes(d_out, d_in, T, r))
+
+
+def qlora_status_string(status: int) -> str:
+    return _lib.qlora_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+@dataclass
+class NF4Weight:
+    """A quantized frozen weight: the three buffers of qlora_nf4_weight plus its shape."""
+    d_out: int
+    d_in: int
+    codes: torch.Tensor    # uint8 [d_out*d_in/2]
+    qscale: torch.Tensor   # uint8 [d_out*d_in/64]
+    smax: torch.Tensor     # float32 [ceil(d_out*d_in/64/256)]
+
+    def _c(self):
+        return _Nf4Weight(self.d_out, self.d_in, self.codes.data_ptr(), self.qscale.data_ptr(),
+                          self.smax.data_ptr())
+
+    @staticmethod
+    def empty(d_out: int, d_in: int, device) -> "NF4Weight":
+        n = d_out * d_in
+        nb = n // BLOCK
+        ng = (nb + GROUP - 1) // GROUP
+        # 16-byte aligned allocations (torch's caching allocator aligns to >= 512 bytes)
+        return NF4Weight(d_out, d_in,
+                         torch.empty(n // 2, dtype=torch.uint8, device=device),
+                         torch.empty(nb, dtype=torch.uint8, device=device),
+                         torch.empty(ng, dtype=torch.float32, device=device))
+
+
+_workspaces: dict = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace cached per device (the library leaves its counters zero after each call)."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 1 << 20)
+        if ws is not None:
+            size = max(size, 2 * ws.numel())
+        torch.cuda.synchronize(dev)
+        ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t
+
+
+def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.Tensor | None = None) -> NF4Weight:
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
+    if W.dtype == torch.float32:
+        dt = F32
+    elif W.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
+    d_out, d_in = W.shape
+    if out is None:
+        out = NF4Weight.empty(d_out, d_in, W.device)
+    cw = out._c()
+    _check(_lib.qlora_quantize(_ptr(W), dt, ctypes.byref(cw), _ptr(flags), _stream(W.device)), "qlora_quantize")
+    return out
+
+
+def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:
+    out = torch.empty(w.d_out, w.d_in, dtype=dtype, device=w.codes.device)
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    cw = w._c()
+    _check(_lib.qlora_dequantize(ctypes.byref(cw), dt, _ptr(out), _stream(out.device)), "qlora_dequantize")
+    return out
+
+
+def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
+                  save_u: bool = False, h: torch.Tensor | None = None):
+    """h = x W_hat^T + (alpha/r) (x A^T) B^T. Returns (h, u) with u float32 [T, r] if save_u else None."""
+    x = _bits(x)
+    T = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if A is not None:
+        _bits(A), _bits(B)
+    if h is None:
+        h = torch.empty(T, w.d_out, dtype=torch.bfloat16, device=x.device)
+    u = torch.empty(T, r, dtype=torch.float32, device=x.device) if (save_u and r > 0) else None
+    nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
+    ws = workspace(x.device, nbytes)
+    cw = w._c()
+    _check(_lib.qlora_forward(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
+                              _ptr(ws), ws.numel(), _stream(x.device)), "qlora_forward")
+    return h, u
+
+
+def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor | None,
+                   B: torch.Tensor | None, alpha: float, u_saved: torch.Tensor | None = None,
+                   need_dx: bool = True, need_dA: bool = True, need_dB: bool = True):
+    """Returns (dX bf16 [T, d_in] | None, dA f32 [r, d_in] | None, dB f32 [d_out, r] | None)."""
+    dY = _bits(dY)
+    T = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    dX = torch.empty(T, w.d_in, dtype=torch.bfloat16, device=dev) if need_dx else None
+    dA = torch.empty(r, w.d_in, dtype=torch.float32, device=dev) if (need_dA and r > 0) else None
+    dB = torch.empty(w.d_out, r, dtype=torch.float32, device=dev) if (need_dB and r > 0) else None
+    nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
+    ws = workspace(dev, nbytes)
+    cw = w._c()
+    _check(_lib.qlora_backward(ctypes.byref(cw), _ptr(x), _ptr(dY), T, _ptr(A), _ptr(B), r, alpha, _ptr(u_saved),
+                               _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)), "qlora_backward")
+    return dX, dA, dB

@@ -1,0 +1,146 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA frozen-NF4 linear layer.
+ *
+ * The layer is the two-term forward of "QLoRA는 어떻게 65B 모델을 GPU 한 장에
+ * 올렸나" (section "QLoRA의 수식"):
+ *
+ *     h = dequant(W_NF4, c_block) x + (alpha/r) B A x
+ *
+ * with tokens as rows: x [T, d_in], W [d_out, d_in], A [r, d_in], B [d_out, r],
+ * h [T, d_out]. The base weight is stored as 4-bit NF4 indices in blocks of 64
+ * with a per-block absmax scale that is itself re-quantized to 8 bits against a
+ * per-group float32 maximum ("48GB GPU Fine-Tuning a 65B Model", section
+ * "Quantization Keeps the Patterns and Reduces Bits per Number"; the
+ * double-quantization paragraph and reconstruction equation of the first page,
+ * section "메모리 회계"). Compute is bf16 with float32 accumulation.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP), row-major, 16-byte aligned,
+ *     except where a comment says "host".
+ *   - The library allocates no memory. The caller owns every buffer; inputs must
+ *     stay alive and unmodified until the stream work has completed.
+ *   - Work is enqueued asynchronously on `stream` (0 = the legacy default stream).
+ *   - Arguments are validated on the host before anything is enqueued. On any
+ *     error the call returns a negative status and writes no output byte.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Calls that run concurrently (other streams or threads) must not share a
+ *     workspace.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_BLOCK 64   /* weights per absmax block                          */
+#define QLORA_GROUP 256  /* blocks per double-quant group (one float32 S_g)    */
+#define QLORA_MAX_RANK 256
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,      /* a required pointer is NULL                     */
+  QLORA_ERR_SHAPE = -2,     /* d_in % 64 != 0, a size < 1, or r out of range  */
+  QLORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned               */
+  QLORA_ERR_WORKSPACE = -4, /* ws_bytes < qlora_workspace_bytes(...)          */
+  QLORA_ERR_DTYPE = -5,     /* unknown dtype enum                             */
+  QLORA_ERR_HIP = -6        /* a kernel launch failed                         */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+/*
+ * A quantized frozen weight W [d_out, d_in] (d_in % 64 == 0), n = d_out*d_in,
+ * nblocks = n/64, ngroups = ceil(nblocks/256). Blocks are 64 consecutive
+ * weights of the row-major flattening (so a block never straddles a row);
+ * groups are 256 consecutive blocks (they may straddle rows).
+ *   codes  [n/2]      u8   two 4-bit codebook indices per byte, element 2m in the
+ *                          low nibble of byte m
+ *   qscale [nblocks]  u8   8-bit code q2 of each block scale, 0..255
+ *   smax   [ngroups]  f32  per-group maximum S_g of the block scales
+ * Restored weight: w_hat = bf16( c[q] * (q2/256 * S_g) ), each product rounded
+ * to float32 first (reconstruction equation of the "메모리 회계" section).
+ */
+typedef struct {
+  int64_t d_out;
+  int64_t d_in;
+  uint8_t *codes;
+  uint8_t *qscale;
+  float *smax;
+} qlora_nf4_weight;
+
+/*
+ * Quantize W once (a load-time step in the pages' training snippet, "무엇을
+ * 돌렸나" of the GPU-fit page).
+ *   W        device, [d_out, d_in], float32 or bf16 (w_dtype)
+ *   out      host struct naming the three output buffers (sizes above)
+ *   flags    device u32, nullable; bit 0 is OR-ed in when a non-finite weight is
+ *            seen (the codes are then unspecified)
+ * Per block: s = max|w|; each w/s (IEEE float32 divide) takes the index of the
+ * nearest NF4 level, ties to the lower index; s = 0 gives index 7 (exact zero).
+ * Per group: S = max s; q2 = min(255, rint(fl32(s/S)*256)); S = 0 gives q2 = 0.
+ * Bit-exact with the CPU oracle.
+ */
+int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint32_t *flags,
+                   hipStream_t stream);
+
+/*
+ * Restore the full weight (for checking, merging or export).
+ *   out  device, [d_out, d_in], float32 (the unrounded float32 product) or bf16.
+ */
+int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStream_t stream);
+
+/*
+ * Forward h = x W_hat^T + (alpha/r) (x A^T) B^T ("QLoRA의 수식").
+ *   x      device bf16 [T, d_in]
+ *   A, B   device bf16 [r, d_in], [d_out, r]; both NULL, or r == 0, means base only
+ *   h      device bf16 [T, d_out] (overwritten)
+ *   u_out  device f32 [T, r], nullable: receives u = x A^T for the backward
+ *   ws     device workspace of at least qlora_workspace_bytes(d_out, d_in, T, r)
+ *          bytes; it must be zero-filled before its first use, and every call
+ *          leaves its counter region zero again.
+ * T <= 16 runs the weight-streaming (GEMV) kernel; larger T the MFMA GEMM.
+ */
+int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A,
+                  const uint16_t *B, int32_t r, float alpha, uint16_t *h, float *u_out, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward through the frozen restored weight ("QLoRA의 수식", "명제 1"):
+ *   v  = dY B
+ *   dX = dY W_hat + (alpha/r) v A        device bf16 [T, d_in], nullable
+ *   dA = (alpha/r) v^T x                 device f32 [r, d_in], nullable, overwritten
+ *   dB = (alpha/r) dY^T u,  u = x A^T    device f32 [d_out, r], nullable, overwritten
+ *   u_saved  device f32 [T, r] from qlora_forward's u_out, nullable (then recomputed)
+ * The codes/qscale/smax buffers are only read: no gradient flows into W.
+ * With r == 0 only dX is produced (dA, dB must be NULL).
+ */
+int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t *dY, int64_t T,
+                   const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                   const float *u_saved, uint16_t *dX, float *dA, float *dB, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the quantized weight: n/2 + n/64 + 4*ceil(n/16384). */
+size_t qlora_storage_bytes(int64_t d_out, int64_t d_in);
+
+/* Workspace bytes sufficient for both qlora_forward and qlora_backward at these sizes. */
+size_t qlora_workspace_bytes(int64_t d_out, int64_t d_in, int64_t T, int32_t r);
+
+/* Host: the 16 float32 NF4 levels, ascending (c[0] = -1, c[7] = 0, c[15] = 1). */
+void qlora_nf4_codebook(float out[16]);
+
+/* Host: the 15 float32 decision thresholds (smallest float32 above each level midpoint). */
+void qlora_nf4_thresholds(float out[15]);
+
+/* Host: static text for a status code. */
+const char *qlora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,224 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bit-exact: packed codes, scale codes, group maxima, restored weights (float32 and
+bf16). Within tolerance (see gpu_common): h, dX, dA, dB. Shapes span several
+tiles and ragged tails of every kernel: T in {1, 4, 16} takes the weight-streaming
+kernel, larger T the MFMA GEMM; d_out not a multiple of the 64/256 row tiles;
+d_in not a multiple of the 256-wide K segments; groups of 256 blocks that straddle
+rows and a short last group.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import Case, assert_close, bits_to_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("bit_quantized_finetuning_amd.qlora")
+
+
+def _quantize_and_compare(case):
+    d = case.device_inputs()
+    w = q.qlora_quantize(d["W"])
+    torch.cuda.synchronize()
+    codes, q2, S, w32, wb = case.oracle_quant()
+    assert np.array_equal(w.codes.cpu().numpy(), codes), "packed codes differ"
+    assert np.array_equal(w.qscale.cpu().numpy(), q2), "scale codes differ"
+    assert np.array_equal(w.smax.cpu().numpy().view(np.uint32), S.view(np.uint32)), "group maxima differ"
+    return w, d
+
+
+# ---------------------------------------------------------------------------
+# quantize / dequantize: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,wdtype", [
+    (1024, 1024, "f32"),     # single-linear workload
+    (16, 64, "f32"),         # smallest legal weight: one block per row, one short group
+    (48, 192, "f32"),
+    (80, 320, "f32"),        # 400 blocks: groups straddle rows, short last group
+    (32, 5120, "bf16"),      # bf16 weights, 80 blocks per row
+    (4096, 4096, "f32"),     # LLaMA-7B q_proj shape
+])
+def test_quantize_bit_exact(d_out, d_in, wdtype):
+    say(f"quantize {d_out}x{d_in} {wdtype}")
+    _quantize_and_compare(Case(d_out, d_in, 0, 1, cfg=101, wdtype=wdtype))
+
+
+def test_quantize_adversarial_blocks():
+    """Midpoint ties and their float32 neighbours, zero blocks, an outlier group, all-negative blocks."""
+    say("quantize adversarial")
+    mids = oracle.nf4_midpoints_f64()
+    vals = []
+    for m in mids:
+        f = np.float32(m)
+        vals += [f, np.nextafter(f, np.float32(-1)), np.nextafter(f, np.float32(1))]
+        vals += [-f, np.nextafter(-f, np.float32(-1)), np.nextafter(-f, np.float32(1))]
+    vals = np.array(vals, dtype=np.float32)
+    rows = []
+    for i in range(0, vals.size, 63):
+        blk = np.zeros(64, dtype=np.float32)
+        chunk = vals[i:i + 63]
+        blk[:chunk.size] = chunk
+        blk[63] = 1.0                       # absmax 1 -> w/s == w exactly
+        rows.append(blk)
+    W = np.zeros((16, 64 * 8), dtype=np.float32)
+    flat = np.concatenate(rows)
+    W.reshape(-1)[:flat.size] = flat
+    W[5, :] = 0.0                           # zero blocks
+    W[6, :64] = -np.abs(np.linspace(0.01, 0.5, 64, dtype=np.float32))
+    W[9, :] = 1e-3
+    W[9, 70] = 10.0                         # outlier: small blocks of the group go to q2 = 0
+    W[12, :64] = np.float32(1e-30)          # tiny (near-denormal ratios stay normal)
+    case = Case(16, 512, 0, 1, cfg=102)
+    case.W = W
+    w, d = _quantize_and_compare(case)
+    out = q.qlora_dequantize(w, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), case.oracle_quant()[3].view(np.uint32))
+
+
+@pytest.mark.parametrize("d_out,d_in", [(1024, 1024), (80, 320), (272, 5120)])
+def test_dequantize_bit_exact(d_out, d_in):
+    say(f"dequantize {d_out}x{d_in}")
+    case = Case(d_out, d_in, 0, 1, cfg=103)
+    w, _ = _quantize_and_compare(case)
+    o32 = q.qlora_dequantize(w, torch.float32)
+    ob = q.qlora_dequantize(w, torch.bfloat16)
+    torch.cuda.synchronize()
+    _, _, _, w32, wb = case.oracle_quant()
+    assert np.array_equal(o32.cpu().numpy().view(np.uint32), w32.view(np.uint32)), "float32 restore differs"
+    assert np.array_equal(ob.float().cpu().numpy().view(np.uint32), wb.view(np.uint32)), "bf16 restore differs"
+
+
+def test_quantize_flags_non_finite():
+    say("quantize non-finite flag")
+    W = torch.zeros(16, 64, device="cuda")
+    W[3, 7] = float("inf")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q.qlora_quantize(W, flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & 1
+    flags.zero_()
+    q.qlora_quantize(torch.ones(16, 64, device="cuda"), flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# forward / backward: tolerance
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # d_out, d_in, r
+    (1024, 1024, 8),      # single-linear workload shape
+    (80, 192, 16),        # ragged rows / K segments
+    (272, 320, 64),
+    (16, 64, 0),          # base only, minimal
+    (528, 1344, 256),     # maximum rank
+]
+TOKENS = [1, 4, 16, 17, 100, 300]
+
+
+@pytest.mark.parametrize("d_out,d_in,r", SHAPES)
+@pytest.mark.parametrize("T", TOKENS)
+def test_forward_parity(d_out, d_in, r, T):
+    say(f"forward {d_out}x{d_in} r={r} T={T}")
+    case = Case(d_out, d_in, r, T, cfg=104)
+    w, d = _quantize_and_compare(case)
+    h, u = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha, save_u=True)
+    torch.cuda.synchronize()
+    h_ref, u_ref = case.oracle_forward()
+    assert_close("h", h, h_ref)
+    if r > 0:
+        assert_close("u", u, u_ref)
+
+
+@pytest.mark.parametrize("d_out,d_in,r", SHAPES)
+@pytest.mark.parametrize("T", [1, 16, 100, 300])
+@pytest.mark.parametrize("saved_u", [True, False])
+def test_backward_parity(d_out, d_in, r, T, saved_u):
+    say(f"backward {d_out}x{d_in} r={r} T={T} saved_u={saved_u}")
+    case = Case(d_out, d_in, r, T, cfg=105)
+    w, d = _quantize_and_compare(case)
+    u = None
+    if saved_u and r > 0:
+        _, u = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha, save_u=True)
+    dX, dA, dB = q.qlora_backward(w, d["x"], d["dY"], d["A"], d["B"], case.alpha, u_saved=u)
+    torch.cuda.synchronize()
+    dX_ref, dA_ref, dB_ref = case.oracle_backward()
+    assert_close("dX", dX, dX_ref)
+    if r > 0:
+        assert_close("dA", dA, dA_ref)
+        assert_close("dB", dB, dB_ref)
+    else:
+        assert dA is None and dB is None
+
+
+@pytest.mark.parametrize("T", [4, 300])
+def test_zero_B_gives_base_output_exactly(T):
+    """B = 0: h is bit-identical to the adapter-free call (48GB page: B = 0 at init leaves the model unchanged)."""
+    say(f"zero-B T={T}")
+    case = Case(272, 320, 64, T, cfg=106)
+    w, d = _quantize_and_compare(case)
+    h0, _ = q.qlora_forward(w, d["x"], d["A"], torch.zeros_like(d["B"]), case.alpha)
+    hb, _ = q.qlora_forward(w, d["x"], None, None, case.alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), hb.view(torch.int16))
+
+
+def test_zero_weight_leaves_adapter_term():
+    say("zero weight")
+    case = Case(64, 128, 8, 20, cfg=107)
+    case.W = np.zeros_like(case.W)
+    w, d = _quantize_and_compare(case)
+    assert int(w.codes.cpu().unique().numel()) == 1 and int(w.codes[0].item()) == 0x77
+    h, _ = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha)
+    torch.cuda.synchronize()
+    assert_close("h", h, case.oracle_forward()[0])
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_no_gradient_into_weight(T):
+    say(f"frozen weight T={T}")
+    case = Case(272, 320, 64, T, cfg=108)
+    w, d = _quantize_and_compare(case)
+    before = (w.codes.clone(), w.qscale.clone(), w.smax.clone())
+    q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha)
+    q.qlora_backward(w, d["x"], d["dY"], d["A"], d["B"], case.alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(before[0], w.codes) and torch.equal(before[1], w.qscale)
+    assert torch.equal(before[2].view(torch.int32), w.smax.view(torch.int32))
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_deterministic_reruns(T):
+    say(f"determinism T={T}")
+    case = Case(1024, 1024, 64, T, cfg=109)
+    w, d = _quantize_and_compare(case)
+    outs = []
+    for _ in range(2):
+        h, u = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha, save_u=True)
+        g = q.qlora_backward(w, d["x"], d["dY"], d["A"], d["B"], case.alpha, u_saved=u)
+        torch.cuda.synchronize()
+        outs.append([h.clone(), u.clone()] + [t.clone() for t in g])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_error_leaves_outputs_untouched():
+    say("error path sentinel")
+    case = Case(64, 128, 8, 4, cfg=110)
+    w, d = _quantize_and_compare(case)
+    h = torch.full((4, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    cw = w._c()
+    import ctypes
+    st = q.lib.qlora_forward(ctypes.byref(cw), d["x"].data_ptr(), 4, d["A"].data_ptr(), d["B"].data_ptr(), 8,
+                             16.0, h.data_ptr(), None, q.workspace("cuda", 1 << 20).data_ptr(), 16, None)
+    torch.cuda.synchronize()
+    assert st == -4
+    assert bool((h == 7.0).all())
