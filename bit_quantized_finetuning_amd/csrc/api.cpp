@@ -10,7 +10,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/qlora.h"
+#include "qlora.h"
 #include "kernels.h"
 
 using namespace qlora;
@@ -67,6 +67,10 @@ const Nf4Consts &consts() {
   return t.c;
 }
 
+// Per-tile buffer ranges stay below 2^31 bytes with these bounds.
+constexpr int64_t kMaxDim = (int64_t)1 << 20;
+constexpr int64_t kMaxTokens = (int64_t)1 << 24;
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -76,7 +80,7 @@ int validate_weight(const qlora_nf4_weight *W) {
   if (!W || !W->codes || !W->qscale || !W->smax) return QLORA_ERR_NULL;
   if (W->d_out < 1 || W->d_in < QLORA_BLOCK || W->d_in % QLORA_BLOCK != 0 || W->d_out % 16 != 0)
     return QLORA_ERR_SHAPE;
-  if (W->d_out > (int64_t)1 << 31 || W->d_in > (int64_t)1 << 31) return QLORA_ERR_SHAPE;
+  if (W->d_out > kMaxDim || W->d_in > kMaxDim) return QLORA_ERR_SHAPE;
   if (!aligned16(W->codes) || !aligned16(W->qscale) || !aligned16(W->smax)) return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
@@ -95,7 +99,7 @@ int lora_small_ksplit(int64_t T, int64_t K) {
 // counts arriving workgroups resets its counters before it exits, and the calls
 // of one stream run one kernel at a time.
 struct Layout {
-  size_t sx, u, v, bt, partial, total;
+  size_t sx, su32, u, v, bt, partial, total;
 };
 
 Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
@@ -105,6 +109,8 @@ Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
   size_t off = align256((size_t)kMaxCounters * sizeof(uint32_t));
   L.sx = off;
   off = align256(off + (size_t)T16 * rp * 2);
+  L.su32 = off;
+  off = align256(off + (size_t)gemv_ksplit(d_in) * 16 * rp * 4);
   L.u = off;
   off = align256(off + (size_t)T * r * 4);
   L.v = off;
@@ -112,7 +118,6 @@ Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
   L.bt = off;
   off = align256(off + (size_t)r * d_out * 2);
   size_t pf = 0;
-  if (T <= 16) pf = std::max(pf, (size_t)ceil_div(d_out, 64) * gemv_ksplit(d_out, d_in) * 1024);
   if (r > 0) {
     pf = std::max(pf, (size_t)ceil_div(T, 16) * lora_small_ksplit(T, std::max(d_in, d_out)) * 16 * rp);
     pf = std::max(pf, lora_grad_partial_floats(r, d_in, T));
@@ -194,7 +199,7 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   if (s) return s;
   if (!x || !h) return QLORA_ERR_NULL;
   if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
-  if (T > (int64_t)1 << 24) return QLORA_ERR_SHAPE;
+  if (T > kMaxTokens) return QLORA_ERR_SHAPE;
   if (!A && !B) r = 0;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(x) || !aligned16(h) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
@@ -209,20 +214,19 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   const Nf4Consts &c = consts();
   const int rp = rank_pad(r);
   const float sc = r > 0 ? alpha / (float)r : 0.f;
+  if (T <= 16)
+    return hip_status(launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, A, B, r, rp, sc, h, u_out,
+                                      at<float>(ws, L.su32), at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4), c,
+                                      stream));
   uint16_t *su = at<uint16_t>(ws, L.sx);
   float *partial = at<float>(ws, L.partial);
   hipError_t e = hipSuccess;
   if (r > 0) {
     const int ks = lora_small_ksplit(T, d_in);
-    e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks,
-                          stream);
+    e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
-  if (T <= 16)
-    e = launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
-                        at<uint32_t>(ws, 0), gemv_ksplit(d_out, d_in), c, stream);
-  else
-    e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, c, stream);
+  e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, c, stream);
   return hip_status(e);
 }
 
@@ -233,7 +237,7 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
   if (s) return s;
   if (!dY) return QLORA_ERR_NULL;
   if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
-  if (T > (int64_t)1 << 24) return QLORA_ERR_SHAPE;
+  if (T > kMaxTokens) return QLORA_ERR_SHAPE;
   if (!A && !B) r = 0;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (r == 0 && (dA || dB)) return QLORA_ERR_SHAPE;

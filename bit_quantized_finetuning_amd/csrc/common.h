@@ -20,8 +20,12 @@ constexpr int kBlock = 64;
 constexpr int kGroup = 256;
 // Split reductions count arriving workgroups per output tile in a fixed region
 // at the start of the workspace (zero before first use, left zero by every
-// kernel). A kernel whose tile count exceeds it runs without a split.
+// kernel). A kernel whose tile count exceeds kMaxTileCounters runs without a
+// split. The last kSyncWords words of the region are the skinny forward's
+// producer/consumer handshake.
 constexpr int64_t kMaxCounters = 16384;
+constexpr int64_t kSyncWords = 4;
+constexpr int64_t kMaxTileCounters = kMaxCounters - kSyncWords;
 
 // Codebook and decision thresholds, passed to kernels by value (kernel arguments
 // live in SGPRs; they are only ever indexed with compile-time constants).
@@ -90,47 +94,31 @@ __device__ __forceinline__ uint32_t lookup4(const uint32_t pl[4], uint32_t sel, 
   return perm(b, a, merge);
 }
 
-// Expand one dword of packed codes (8 nibbles: element 2i in the low nibble of
-// byte i) into 8 restored bf16 weights, returned in the slot order
-//   [e0, e2, e4, e6, e1, e3, e5, e7]
-// (the partner MFMA operand is permuted to the same order, see x_slots()).
+// Expand one 32-bit word of packed codes into 8 restored bf16 weights in
+// element order. Packing: the word covers 8 consecutive weights e0..e7 and byte
+// i (i = 0..3) holds e_i in its low nibble and e_(i+4) in its high nibble, so
+// the low nibbles select e0..e3 and the high nibbles e4..e7 with the same byte
+// lanes, and one byte interleave of the low/high planes yields bf16 pairs.
+// Cost: 7 selector ops + 12 table perms + 4 interleave perms per 8 weights.
 __device__ __forceinline__ u32x4 expand8(const Nf4Planes &t, uint32_t c) {
-  const uint32_t se = c & 0x07070707u;
-  const uint32_t me = ((c >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t so = (c >> 4) & 0x07070707u;
-  const uint32_t mo = ((c >> 5) & 0x04040404u) | 0x03020100u;
-  const uint32_t lo_e = lookup4(t.lo, se, me);
-  const uint32_t hi_e = lookup4(t.hi, se, me);
-  const uint32_t lo_o = lookup4(t.lo, so, mo);
-  const uint32_t hi_o = lookup4(t.hi, so, mo);
+  const uint32_t sa = c & 0x07070707u;
+  const uint32_t ma = ((c >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t sb = (c >> 4) & 0x07070707u;
+  const uint32_t mb = ((c >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t lo_a = lookup4(t.lo, sa, ma);  // low bytes of e0..e3
+  const uint32_t hi_a = lookup4(t.hi, sa, ma);
+  const uint32_t lo_b = lookup4(t.lo, sb, mb);  // low bytes of e4..e7
+  const uint32_t hi_b = lookup4(t.hi, sb, mb);
   u32x4 r;
-  r[0] = perm(hi_e, lo_e, 0x05010400u);  // (e0, e2)
-  r[1] = perm(hi_e, lo_e, 0x07030602u);  // (e4, e6)
-  r[2] = perm(hi_o, lo_o, 0x05010400u);  // (e1, e3)
-  r[3] = perm(hi_o, lo_o, 0x07030602u);  // (e5, e7)
+  r[0] = perm(hi_a, lo_a, 0x05010400u);  // (e0, e1)
+  r[1] = perm(hi_a, lo_a, 0x07030602u);  // (e2, e3)
+  r[2] = perm(hi_b, lo_b, 0x05010400u);  // (e4, e5)
+  r[3] = perm(hi_b, lo_b, 0x07030602u);  // (e6, e7)
   return r;
 }
 
-// Same expansion in natural element order (e0,e1), (e2,e3), ... for writing to memory.
-__device__ __forceinline__ u32x4 expand8_natural(const Nf4Planes &t, uint32_t c) {
-  u32x4 s = expand8(t, c);
-  u32x4 r;
-  r[0] = perm(s[2], s[0], 0x05040100u);  // (e0, e1)
-  r[1] = perm(s[2], s[0], 0x07060302u);  // (e2, e3)
-  r[2] = perm(s[3], s[1], 0x05040100u);  // (e4, e5)
-  r[3] = perm(s[3], s[1], 0x07060302u);  // (e6, e7)
-  return r;
-}
-
-// Permute 8 consecutive bf16 (natural order, 4 dwords) into the slot order of expand8().
-__device__ __forceinline__ u32x4 x_slots(u32x4 x) {
-  u32x4 r;
-  r[0] = perm(x[1], x[0], 0x05040100u);  // (x0, x2)
-  r[1] = perm(x[3], x[2], 0x05040100u);  // (x4, x6)
-  r[2] = perm(x[1], x[0], 0x07060302u);  // (x1, x3)
-  r[3] = perm(x[3], x[2], 0x07060302u);  // (x5, x7)
-  return r;
-}
+// Bit offset of element e (0..7) inside its packed 32-bit word.
+__device__ __forceinline__ int nibble_shift(int e) { return 8 * (e & 3) + 4 * (e >> 2); }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -140,9 +128,63 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Global loads of 16 bytes that bypass nothing special; kept as helpers so the
-// kernels read as intent.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads. A buffer resource covers one tile-sized range; a lane whose
+// byte offset is at or past the range reads zeros, so tails need no branches and
+// every load of a loop body can be issued before the first use. Ranges are kept
+// below 2^31 bytes (the callers rebase per tile), so kOOB is always outside.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  const int n = bytes >= 0x7fffffffll ? 0x7fffffff : (int)bytes;
+  // word 3 = 0x00020000: 32-bit data format, the raw-buffer setting for gfx9 parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// Device-coherent variant (sc1): reads data another workgroup published this launch.
+__device__ __forceinline__ u32x4 bld16_dev(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+}
+__device__ __forceinline__ uint32_t bld32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld32_dev(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16);
+}
+__device__ __forceinline__ uint32_t bld8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup exchange inside one launch, without cache-wide fences: the
+// producer writes with device-scope (sc1, write-through) stores, waits for them
+// to complete, then bumps a device-scope counter; the consumer that sees the
+// final count reads back with device-scope loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev_u32(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every load and store this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace qlora

@@ -47,67 +47,65 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const uint8_t *__restrict__ co
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t *As = smem;                        // [2][kBM][kAP]
   uint16_t *Bs = smem + 2 * kBM * kAP;        // [2][kBN][kAP]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
   const int64_t KB = d_in / kBlock;
   const int nk_main = (int)KB;
   const int nk_lora = r > 0 ? (r_pad + kBK - 1) / kBK : 0;
 
-  // x tile loader: 8 threads per row, 8 rows apart per step
-  const int xr = tid >> 3, xc = (tid & 7) * 8;
+  // Buffer ranges of this tile (rows past T / d_out read zeros).
+  const int64_t mrows = T - m0 < kBM ? T - m0 : kBM;
+  const int64_t nrows = d_out - n0 < kBN ? d_out - n0 : kBN;
+  const rsrc_t xr = make_rsrc(x + m0 * d_in, mrows * d_in * 2);
+  const rsrc_t cr = make_rsrc(codes + n0 * (d_in / 2), nrows * (d_in / 2));
+  const rsrc_t qr = make_rsrc(qscale + n0 * KB, nrows * KB);
+  const rsrc_t sr = make_rsrc(smax, ((d_out * KB + kGroup - 1) / kGroup) * 4);
+
+  // x tile loader: 8 threads per row, 32 rows apart per step
+  const int xr_ = tid >> 3, xc = (tid & 7) * 8;
   u32x4 xa[8];
   u32x4 cw0, cw1;
-  float sh;
+  uint32_t q2;
+  float S;
 
   auto load_main = [&](int kt) {
     const int64_t k0 = (int64_t)kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      xa[i] = u32x4{0u, 0u, 0u, 0u};
-      if (m < T) xa[i] = ld16(x + m * d_in + k0 + xc);
-    }
-    const int64_t n = n0 + tid;
-    cw0 = cw1 = u32x4{0u, 0u, 0u, 0u};
-    sh = 0.f;
-    if (n < d_out) {
-      const uint8_t *cp = codes + n * (d_in / 2) + (int64_t)kt * (kBlock / 2);
-      cw0 = ld16(cp);
-      cw1 = ld16(cp + 16);
-      const int64_t blk = n * KB + kt;
-      sh = restore_scale(qscale[blk], smax[blk >> 8]);
-    }
+    for (int i = 0; i < 8; ++i) xa[i] = bld16(xr, (uint32_t)(((xr_ + 32 * i) * d_in + k0 + xc) * 2));
+    const uint32_t coff = (uint32_t)(tid * (d_in / 2) + (int64_t)kt * (kBlock / 2));
+    cw0 = bld16(cr, coff);
+    cw1 = bld16(cr, coff + 16);
+    q2 = bld8(qr, (uint32_t)(tid * KB + kt));
+    S = __uint_as_float(bld32(sr, (uint32_t)((((n0 + tid) * KB + kt) >> 8) * 4)));
   };
   auto store_main = [&](int buf) {
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st16(as + (xr + 32 * i) * kAP + xc, xa[i]);
-    const Nf4Planes t = make_planes(c, sh);
+    for (int i = 0; i < 8; ++i) st16(as + (xr_ + 32 * i) * kAP + xc, xa[i]);
+    const Nf4Planes t = make_planes(c, restore_scale(q2, S));
     uint16_t *bs = Bs + buf * kBN * kAP + tid * kAP;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st16(bs + 8 * m, expand8_natural(t, cw0[m]));
+    for (int m = 0; m < 4; ++m) st16(bs + 8 * m, expand8(t, cw0[m]));
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st16(bs + 32 + 8 * m, expand8_natural(t, cw1[m]));
+    for (int m = 0; m < 4; ++m) st16(bs + 32 + 8 * m, expand8(t, cw1[m]));
   };
   // Adapter K tile: su [T, r_pad] and B [d_out, r], both K-contiguous bf16.
+  const rsrc_t ur = make_rsrc(su + m0 * r_pad, mrows * r_pad * 2);
+  const rsrc_t br = make_rsrc(B + n0 * r, nrows * r * 2);
   auto load_store_lora = [&](int lt, int buf) {
     const int j0 = lt * kBK;
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < T && j0 + xc < r_pad) v = ld16(su + m * r_pad + j0 + xc);
-      st16(as + (xr + 32 * i) * kAP + xc, v);
+      const uint32_t off = j0 + xc < r_pad ? (uint32_t)(((xr_ + 32 * i) * r_pad + j0 + xc) * 2) : kOOB;
+      st16(as + (xr_ + 32 * i) * kAP + xc, bld16(ur, off));
     }
-    const int64_t n = n0 + tid;
     uint16_t *bs = Bs + buf * kBN * kAP + tid * kAP;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < d_out && j0 + 8 * q < r) v = ld16(B + n * r + j0 + 8 * q);
-      st16(bs + 8 * q, v);
+      const uint32_t off = j0 + 8 * q < r ? (uint32_t)((tid * r + j0 + 8 * q) * 2) : kOOB;
+      st16(bs + 8 * q, bld16(br, off));
     }
   };
 
@@ -192,68 +190,73 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint8_t *__restrict__ cod
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t *As = smem;                      // [2][kBM][kAP]   dY tile [t][o]
   uint16_t *Bt = smem + 2 * kBM * kAP;      // [2][kBK][kBTP]  W_hat tile [o][i]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;  // n = input feature i
   const int64_t KB = d_in / kBlock;
   const int nk_main = (int)((d_out + kBK - 1) / kBK);
   const int nk_lora = r > 0 ? (r_pad + kBK - 1) / kBK : 0;
 
-  const int xr = tid >> 3, xc = (tid & 7) * 8;
+  const int64_t mrows = T - m0 < kBM ? T - m0 : kBM;
+  const rsrc_t yr = make_rsrc(dY + m0 * d_out, mrows * d_out * 2);
+  const rsrc_t sr = make_rsrc(smax, ((d_out * KB + kGroup - 1) / kGroup) * 4);
+
+  const int xr_ = tid >> 3, xc = (tid & 7) * 8;
   const int wo = tid >> 2, wb = tid & 3;  // weight tile: row o, block b (64 columns)
+  const int64_t kblk = n0 / kBlock + wb;
   u32x4 xa[8];
   u32x4 cw0, cw1;
-  float sh;
+  uint32_t q2;
+  float S;
 
   auto load_main = [&](int kt) {
     const int64_t k0 = (int64_t)kt * kBK;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      xa[i] = u32x4{0u, 0u, 0u, 0u};
-      if (m < T && k0 + xc < d_out) xa[i] = ld16(dY + m * d_out + k0 + xc);
+      const uint32_t off = k0 + xc < d_out ? (uint32_t)(((xr_ + 32 * i) * d_out + k0 + xc) * 2) : kOOB;
+      xa[i] = bld16(yr, off);
     }
-    const int64_t o = k0 + wo;
-    const int64_t kblk = n0 / kBlock + wb;
-    cw0 = cw1 = u32x4{0u, 0u, 0u, 0u};
-    sh = 0.f;
-    if (o < d_out && kblk < KB) {
-      const uint8_t *cp = codes + o * (d_in / 2) + kblk * (kBlock / 2);
-      cw0 = ld16(cp);
-      cw1 = ld16(cp + 16);
-      const int64_t blk = o * KB + kblk;
-      sh = restore_scale(qscale[blk], smax[blk >> 8]);
-    }
+    // weight rows k0..k0+63 of this k tile, 4 blocks of columns per row
+    const int64_t orows = d_out - k0 < kBK ? d_out - k0 : kBK;
+    const rsrc_t cr = make_rsrc(codes + k0 * (d_in / 2), orows * (d_in / 2));
+    const rsrc_t qr = make_rsrc(qscale + k0 * KB, orows * KB);
+    const bool ok = kblk < KB;
+    const uint32_t coff = ok ? (uint32_t)(wo * (d_in / 2) + kblk * (kBlock / 2)) : kOOB;
+    cw0 = bld16(cr, coff);
+    cw1 = bld16(cr, coff + 16);
+    q2 = bld8(qr, ok ? (uint32_t)(wo * KB + kblk) : kOOB);
+    S = __uint_as_float(bld32(sr, ok ? (uint32_t)((((k0 + wo) * KB + kblk) >> 8) * 4) : kOOB));
   };
   auto store_main = [&](int buf) {
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st16(as + (xr + 32 * i) * kAP + xc, xa[i]);
-    const Nf4Planes t = make_planes(c, sh);
+    for (int i = 0; i < 8; ++i) st16(as + (xr_ + 32 * i) * kAP + xc, xa[i]);
+    const Nf4Planes t = make_planes(c, restore_scale(q2, S));
     uint16_t *bt = Bt + buf * kBK * kBTP + wo * kBTP + wb * 64;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st16(bt + 8 * m, expand8_natural(t, cw0[m]));
+    for (int m = 0; m < 4; ++m) st16(bt + 8 * m, expand8(t, cw0[m]));
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st16(bt + 32 + 8 * m, expand8_natural(t, cw1[m]));
+    for (int m = 0; m < 4; ++m) st16(bt + 32 + 8 * m, expand8(t, cw1[m]));
   };
+  const rsrc_t vr = make_rsrc(sv + m0 * r_pad, mrows * r_pad * 2);
+  const rsrc_t ar = make_rsrc(A, (int64_t)r * d_in * 2);
   auto load_store_lora = [&](int lt, int buf) {
     const int j0 = lt * kBK;
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + xr + 32 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < T && j0 + xc < r_pad) v = ld16(sv + m * r_pad + j0 + xc);
-      st16(as + (xr + 32 * i) * kAP + xc, v);
+      const uint32_t off = j0 + xc < r_pad ? (uint32_t)(((xr_ + 32 * i) * r_pad + j0 + xc) * 2) : kOOB;
+      st16(as + (xr_ + 32 * i) * kAP + xc, bld16(vr, off));
     }
     // A rows j0..j0+63, columns n0..n0+255
     uint16_t *bt = Bt + buf * kBK * kBTP;
-    for (int q = tid; q < kBK * (kBN / 8); q += 256) {
-      const int jr = q / (kBN / 8), cc = (q % (kBN / 8)) * 8;
+#pragma unroll
+    for (int q = 0; q < kBK * (kBN / 8) / 256; ++q) {
+      const int e = q * 256 + tid;
+      const int jr = e / (kBN / 8), cc = (e % (kBN / 8)) * 8;
       const int64_t j = j0 + jr, i = n0 + cc;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < r && i < d_in) v = ld16(A + j * d_in + i);
-      st16(bt + jr * kBTP + cc, v);
+      const uint32_t off = (j < r && i < d_in) ? (uint32_t)((j * d_in + i) * 2) : kOOB;
+      st16(bt + jr * kBTP + cc, bld16(ar, off));
     }
   };
 

@@ -14,7 +14,8 @@
 // These products are HBM-bound on their own (arithmetic intensity ~ r flop per
 // byte). Tokens are split across workgroups; the last workgroup of an output
 // tile (device-scope counter) adds the float32 partial tiles in split order, so
-// the result is deterministic.
+// the result is deterministic. Partials travel through device-scope stores and
+// loads (no cache-wide fence); operand tails are read as zeros by buffer loads.
 #include "kernels.h"
 
 namespace qlora {
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
   __shared__ __attribute__((aligned(16))) uint16_t Ph[kGT * kGP], Pl[kPf32 ? kGT * kGP : 1];
   __shared__ __attribute__((aligned(16))) uint16_t Qh[kGT * kGP], Ql[kQf32 ? kGT * kGP : 1];
   __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave & 1, wn = wave >> 1;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int64_t m0 = (int64_t)(tile / tiles_n) * kGT, n0 = (int64_t)(tile % tiles_n) * kGT;
@@ -39,30 +40,37 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
 
   const int lr = tid >> 2, lc = (tid & 3) * 16;  // loader: token row, 16 columns
 
-  auto stage = [&](const void *src, bool f32, int64_t cols, int64_t c0, int64_t t, uint16_t *hi, uint16_t *lo) {
+  // Stage rows t0..t0+63 of a token-major operand (cols wide) as bf16 (hi [+ lo]).
+  auto stage = [&](const void *src, bool f32, int64_t cols, int64_t c0, int64_t t0, uint16_t *hi, uint16_t *lo) {
+    const int esz = f32 ? 4 : 2;
+    const int64_t nrow = T - t0 < kGT ? T - t0 : kGT;
+    const rsrc_t rs = make_rsrc(static_cast<const uint8_t *>(src) + t0 * cols * esz, nrow * cols * esz);
     uint16_t *dh = hi + lr * kGP + lc;
     if (f32) {
-      const float *s = static_cast<const float *>(src);
+      f32x4 v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
         const int64_t cc = c0 + lc + 4 * q;
-        if (t < T && cc < cols) v = *reinterpret_cast<const f32x4 *>(s + t * cols + cc);
-        uint32_t h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
-        uint32_t l0 = pack_bf16x2(v[0] - bf16_lo_to_f32(h0), v[1] - bf16_hi_to_f32(h0));
-        uint32_t l1 = pack_bf16x2(v[2] - bf16_lo_to_f32(h1), v[3] - bf16_hi_to_f32(h1));
+        const u32x4 w = bld16(rs, cc < cols ? (uint32_t)((lr * cols + cc) * 4) : kOOB);
+        v[q] = f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h0 = pack_bf16x2(v[q][0], v[q][1]), h1 = pack_bf16x2(v[q][2], v[q][3]);
+        uint32_t l0 = pack_bf16x2(v[q][0] - bf16_lo_to_f32(h0), v[q][1] - bf16_hi_to_f32(h0));
+        uint32_t l1 = pack_bf16x2(v[q][2] - bf16_lo_to_f32(h1), v[q][3] - bf16_hi_to_f32(h1));
         *reinterpret_cast<u32x2 *>(dh + 4 * q) = u32x2{h0, h1};
         *reinterpret_cast<u32x2 *>(lo + lr * kGP + lc + 4 * q) = u32x2{l0, l1};
       }
     } else {
-      const uint16_t *s = static_cast<const uint16_t *>(src);
+      u32x4 v[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        u32x4 v = {0u, 0u, 0u, 0u};
         const int64_t cc = c0 + lc + 8 * q;
-        if (t < T && cc < cols) v = ld16(s + t * cols + cc);
-        st16(dh + 8 * q, v);
+        v[q] = bld16(rs, cc < cols ? (uint32_t)((lr * cols + cc) * 2) : kOOB);
       }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) st16(dh + 8 * q, v[q]);
     }
   };
 
@@ -80,9 +88,8 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
   };
 
   for (int64_t kt = kb; kt < ke; ++kt) {
-    const int64_t t = kt * kGT + lr;
-    stage(Pv, kPf32, M, m0, t, Ph, Pl);
-    stage(Qv, kQf32, N, n0, t, Qh, Ql);
+    stage(Pv, kPf32, M, m0, kt * kGT, Ph, Pl);
+    stage(Qv, kQf32, N, n0, kt * kGT, Qh, Ql);
     __syncthreads();
 #pragma unroll
     for (int k16 = 0; k16 < kGT / 16; ++k16) {
@@ -109,22 +116,23 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int rm = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    pp[rm * kGT + cn] = acc[e];
+    st_dev(pp + rm * kGT + cn, acc[e]);
   }
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[tile], 1u);
+    const uint32_t prev = add_dev_u32(&counters[tile], 1u);
     is_last = (prev == (uint32_t)ksplit - 1u);
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   const float *pb = partial + (int64_t)tile * ksplit * (kGT * kGT);
   for (int q = tid; q < kGT * kGT / 4; q += 256) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ksplit; ++s)
-      v += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(pb + (int64_t)s * kGT * kGT) + q);
+    for (int s = 0; s < ksplit; ++s) {
+      const float *ps = pb + (int64_t)s * kGT * kGT + 4 * q;
+      v += f32x4{ld_dev(ps), ld_dev(ps + 1), ld_dev(ps + 2), ld_dev(ps + 3)};
+    }
     const int rm = (4 * q) / kGT, rn = (4 * q) % kGT;
     const int64_t m = m0 + rm;
 #pragma unroll
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
       if (m < M && n < N) C[m * N + n] = scale * v[e];
     }
   }
-  if (tid == 0) counters[tile] = 0u;
+  if (tid == 0) st_dev_u32(&counters[tile], 0u);
 }
 
 int lora_grad_tiles(int64_t M, int64_t N) { return (int)(((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT)); }
@@ -141,7 +149,7 @@ int lora_grad_tiles(int64_t M, int64_t N) { return (int)(((M + kGT - 1) / kGT) *
 int lora_grad_ksplit(int64_t M, int64_t N, int64_t T) {
   const int64_t tiles = lora_grad_tiles(M, N);
   const int64_t nkt = (T + kGT - 1) / kGT;
-  if (tiles > kMaxCounters) return 1;
+  if (tiles > kMaxTileCounters) return 1;
   int64_t ks = (512 + tiles - 1) / tiles;
   if (ks > nkt / 2) ks = nkt / 2;
   if (ks < 1) ks = 1;

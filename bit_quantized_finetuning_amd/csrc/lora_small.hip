@@ -11,7 +11,9 @@
 // of a token tile land in a float32 partial buffer and the last workgroup to
 // arrive (device-scope counter) sums them in fixed order, so results do not
 // depend on scheduling. Outputs: float32 out (optional) and the bf16 copy of
-// scale*out that the matmul kernels consume as extra K columns.
+// scale*out that the matmul kernels consume as extra K columns. Loads are raw
+// buffer loads (rows past T and K steps past the slice read zeros), and partials
+// travel through device-scope stores/loads, so no cache-wide fence is needed.
 #include "kernels.h"
 
 namespace qlora {
@@ -25,7 +27,7 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
                                                     uint32_t *__restrict__ counters, int ksplit) {
   __shared__ float red[4][256];
   __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const int split = blockIdx.y;
   const int64_t nk32 = (K + 31) / 32;
@@ -36,23 +38,31 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
 #pragma unroll
   for (int j = 0; j < kMaxNt; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t t = t0 + li;
-  for (int64_t k32 = kb + wave; k32 < ke; k32 += 4) {
-    const int64_t k = k32 * 32 + 8 * g;
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (t < T && k < K) a = ld16(P + t * K + k);
+  const int64_t prow = T - t0 < 16 ? T - t0 : 16;
+  const rsrc_t pr = make_rsrc(P + t0 * K, prow * K * 2);
+  const rsrc_t qr = make_rsrc(Q, (int64_t)r * K * 2);
+  // Two K steps per iteration, all loads first; steps past ke read zeros.
+  for (int64_t k32 = kb + wave; k32 < ke; k32 += 8) {
+    u32x4 a[2], b[2][kMaxNt];
 #pragma unroll
-    for (int j = 0; j < kMaxNt; ++j) {
-      if (j < nt) {
-        const int n = 16 * j + li;
-        u32x4 b = {0u, 0u, 0u, 0u};
-        if (n < r && k < K) b = ld16(Q + (int64_t)n * K + k);
-        acc[j] = mfma16(a, b, acc[j]);
-      }
+    for (int s = 0; s < 2; ++s) {
+      const int64_t kk = k32 + 4 * s;
+      const int64_t k = kk * 32 + 8 * g;
+      const bool ok = kk < ke && k < K;
+      a[s] = bld16(pr, ok ? (uint32_t)((li * K + k) * 2) : kOOB);
+#pragma unroll
+      for (int j = 0; j < kMaxNt; ++j)
+        if (j < nt) b[s][j] = bld16(qr, ok ? (uint32_t)(((16 * j + li) * K + k) * 2) : kOOB);
     }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < kMaxNt; ++j)
+        if (j < nt) acc[j] = mfma16(a[s], b[s][j], acc[j]);
   }
 
   // Reduce the four waves; lane (li, g) of each wave holds rows 4g..4g+3, column li.
+  float *pbase = partial + ((int64_t)blockIdx.x * ksplit + split) * 16 * r_pad;
   for (int j = 0; j < nt; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][lane * 4 + i] = acc[j][i];
@@ -70,26 +80,25 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
           out_bf16[tt * r_pad + col] = (uint16_t)(pack_bf16x2(sv, 0.f) & 0xffffu);
         }
       } else {
-        partial[(((int64_t)blockIdx.x * ksplit + split) * 16 + row) * r_pad + col] = v;
+        st_dev(pbase + row * r_pad + col, v);
       }
     }
     __syncthreads();
   }
   if (ksplit == 1) return;
 
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[blockIdx.x], 1u);
+    const uint32_t prev = add_dev_u32(&counters[blockIdx.x], 1u);
     is_last = (prev == (uint32_t)ksplit - 1u);
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   const float *base = partial + (int64_t)blockIdx.x * ksplit * 16 * r_pad;
   for (int e = tid; e < 16 * r_pad; e += 256) {
     float v = 0.f;
-    for (int s = 0; s < ksplit; ++s) v += __builtin_nontemporal_load(base + (int64_t)s * 16 * r_pad + e);
+    for (int s = 0; s < ksplit; ++s) v += ld_dev(base + (int64_t)s * 16 * r_pad + e);
     const int row = e / r_pad, col = e % r_pad;
     const int64_t tt = t0 + row;
     if (tt < T && col < r && out_f32) out_f32[tt * r + col] = v;
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
       out_bf16[tt * r_pad + col] = (uint16_t)(pack_bf16x2(sv, 0.f) & 0xffffu);
     }
   }
-  if (tid == 0) counters[blockIdx.x] = 0u;
+  if (tid == 0) st_dev_u32(&counters[blockIdx.x], 0u);
 }
 
 // 32x32 tiles through LDS.

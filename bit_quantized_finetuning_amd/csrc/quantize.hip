@@ -7,12 +7,14 @@
 // "메모리 회계"): the block scales are re-coded to 8 bits against their group
 // maximum so that they come back as (q2/256) * S.
 //
-// One workgroup owns one group of 256 blocks (16384 weights): a 16-lane slice
-// reduces the absmax of one 64-weight block (4 weights per lane, 256 contiguous
-// bytes per slice for float32 input), writes that block's 32 bytes of codes, and
-// parks the block scale in LDS; the workgroup then takes the group maximum and
-// writes the 256 scale codes. The kernel is HBM-bound (4 or 2 bytes read per
-// weight, 0.52 written).
+// One workgroup owns one group of 256 blocks (16384 weights). Eight lanes share
+// a block: each loads 8 consecutive weights (32 contiguous bytes of float32, the
+// eight lanes together 256 contiguous bytes), the eight reduce the block absmax
+// with lane shuffles, and each lane emits its weights' codes as one packed
+// 32-bit word. All eight passes' loads are issued before any arithmetic. The
+// block scales wait in LDS for the group maximum, then one thread per block
+// writes its 8-bit scale code. The kernel streams 4 (or 2) bytes in and ~0.52
+// bytes out per weight.
 #include "kernels.h"
 
 namespace qlora {
@@ -22,53 +24,65 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ qscale,
                                                   float *__restrict__ smax, uint32_t *__restrict__ flags,
                                                   Nf4Consts c) {
+  constexpr int esz = kBf16In ? 2 : 4;
+  constexpr int kPasses = kGroup / 32;
   __shared__ float s_blk[kGroup];
   __shared__ float s_red[4];
   const int tid = threadIdx.x;
   const int64_t b0 = (int64_t)blockIdx.x * kGroup;
   const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
-  const int l16 = tid & 15;
-  const int slot = tid >> 4;
-  uint32_t bad = 0;
+  const int l8 = tid & 7;
+  const int slot = tid >> 3;  // 32 blocks per pass
+  const rsrc_t wr = make_rsrc(static_cast<const uint8_t *>(W) + b0 * kBlock * esz, (int64_t)nb * kBlock * esz);
 
-  for (int pass = 0; pass < kGroup / 16; ++pass) {
-    const int b = pass * 16 + slot;
-    if (b >= nb) break;  // uniform across the 16-lane slice
-    const int64_t e0 = (b0 + b) * kBlock + l16 * 4;
-    float w[4];
+  u32x4 raw[kPasses][kBf16In ? 1 : 2];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int b = p * 32 + slot;
+    const uint32_t off = b < nb ? (uint32_t)((b * kBlock + l8 * 8) * esz) : kOOB;
+    raw[p][0] = bld16(wr, off);
+    if (!kBf16In) raw[p][kBf16In ? 0 : 1] = bld16(wr, off + 16);
+  }
+
+  uint32_t bad = 0;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int b = p * 32 + slot;
+    float w[8];
     if (kBf16In) {
-      const u32x2 v = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(W) + e0);
-      w[0] = bf16_lo_to_f32(v[0]);
-      w[1] = bf16_hi_to_f32(v[0]);
-      w[2] = bf16_lo_to_f32(v[1]);
-      w[3] = bf16_hi_to_f32(v[1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] = bf16_lo_to_f32(raw[p][0][e]);
+        w[2 * e + 1] = bf16_hi_to_f32(raw[p][0][e]);
+      }
     } else {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(W) + e0);
-      w[0] = v[0];
-      w[1] = v[1];
-      w[2] = v[2];
-      w[3] = v[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[e] = __uint_as_float(raw[p][0][e]);
+        w[4 + e] = __uint_as_float(raw[p][kBf16In ? 0 : 1][e]);
+      }
     }
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bad |= !__builtin_isfinite(w[i]);
-      m = fmaxf(m, fabsf(w[i]));
+    for (int e = 0; e < 8; ++e) {
+      bad |= !__builtin_isfinite(w[e]);
+      m = fmaxf(m, fabsf(w[e]));
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-    if (l16 == 0) s_blk[b] = m;
-
-    uint32_t packed = 0;
+    for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
+    uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = m > 0.f ? w[i] / m : 0.f;  // IEEE float32 divide
+    for (int e = 0; e < 8; ++e) {
+      const float x = m > 0.f ? w[e] / m : 0.f;  // IEEE float32 divide
       uint32_t q = 0;
 #pragma unroll
       for (int j = 0; j < 15; ++j) q += (x >= c.thr[j]) ? 1u : 0u;
-      packed |= q << (4 * i);
+      word |= q << nibble_shift(e);
     }
-    *reinterpret_cast<uint16_t *>(codes + (b0 + b) * (kBlock / 2) + l16 * 2) = (uint16_t)packed;
+    if (b < nb) {
+      if (l8 == 0) s_blk[b] = m;
+      *reinterpret_cast<uint32_t *>(codes + (b0 + b) * (kBlock / 2) + l8 * 4) = word;
+    }
   }
   __syncthreads();
 
@@ -82,8 +96,8 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   if (tid < nb) {
     uint32_t q2 = 0;
     if (S > 0.f) {
-      const float ratio = s / S;                 // fl32(s / S)
-      const float v = rintf(ratio * 256.f);      // exact scale, ties to even
+      const float ratio = s / S;             // fl32(s / S)
+      const float v = rintf(ratio * 256.f);  // exact scale, ties to even
       q2 = (uint32_t)fminf(v, 255.f);
     }
     qscale[b0 + tid] = (uint8_t)q2;
@@ -92,7 +106,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   if (bad && flags) atomicOr(flags, 1u);
 }
 
-// Restore: one thread per 8 weights (one dword of codes). float32 output is the
+// Restore: one thread per 8 weights (one packed word). float32 output is the
 // unrounded product c[q] * s_hat; bf16 output goes through the same byte-plane
 // table expansion the matmul kernels use, so checking it bit for bit checks
 // their dequantization as well.
@@ -114,13 +128,13 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
     const float sh = restore_scale(qscale[blk], smax[blk >> 8]);
     if (kBf16Out) {
       const Nf4Planes t = make_planes(c, sh);
-      st16(static_cast<uint16_t *>(out) + i * 8, expand8_natural(t, cw));
+      st16(static_cast<uint16_t *>(out) + i * 8, expand8(t, cw));
     } else {
       f32x4 a, b;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        a[e] = cb[(cw >> (4 * e)) & 15u] * sh;
-        b[e] = cb[(cw >> (4 * e + 16)) & 15u] * sh;
+        a[e] = cb[(cw >> nibble_shift(e)) & 15u] * sh;
+        b[e] = cb[(cw >> nibble_shift(e + 4)) & 15u] * sh;
       }
       float *o = static_cast<float *>(out) + i * 8;
       *reinterpret_cast<f32x4 *>(o) = a;

@@ -22,6 +22,8 @@
  *   - Work is enqueued asynchronously on `stream` (0 = the legacy default stream).
  *   - Arguments are validated on the host before anything is enqueued. On any
  *     error the call returns a negative status and writes no output byte.
+ *   - Shapes: d_in % 64 == 0, d_out % 16 == 0, both <= QLORA_MAX_DIM;
+ *     1 <= T <= QLORA_MAX_TOKENS; 0 <= r <= 256 with r % 8 == 0.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Calls that run concurrently (other streams or threads) must not share a
  *     workspace.
@@ -40,6 +42,9 @@ extern "C" {
 #define QLORA_BLOCK 64   /* weights per absmax block                          */
 #define QLORA_GROUP 256  /* blocks per double-quant group (one float32 S_g)    */
 #define QLORA_MAX_RANK 256
+#define QLORA_MAX_DIM (1 << 20)          /* d_in, d_out upper bound            */
+#define QLORA_MAX_TOKENS (1 << 24)       /* T upper bound                      */
+#define QLORA_WS_COUNTER_BYTES 65536     /* zeroed counter region of a workspace */
 
 typedef enum {
   QLORA_OK = 0,
@@ -58,8 +63,9 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
  * nblocks = n/64, ngroups = ceil(nblocks/256). Blocks are 64 consecutive
  * weights of the row-major flattening (so a block never straddles a row);
  * groups are 256 consecutive blocks (they may straddle rows).
- *   codes  [n/2]      u8   two 4-bit codebook indices per byte, element 2m in the
- *                          low nibble of byte m
+ *   codes  [n/2]      u8   4-bit codebook indices; each run of 8 consecutive
+ *                          weights e0..e7 is one little-endian 32-bit word whose
+ *                          byte i holds e_i (low nibble) and e_(i+4) (high nibble)
  *   qscale [nblocks]  u8   8-bit code q2 of each block scale, 0..255
  *   smax   [ngroups]  f32  per-group maximum S_g of the block scales
  * Restored weight: w_hat = bf16( c[q] * (q2/256 * S_g) ), each product rounded
@@ -101,9 +107,13 @@ int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStr
  *   h      device bf16 [T, d_out] (overwritten)
  *   u_out  device f32 [T, r], nullable: receives u = x A^T for the backward
  *   ws     device workspace of at least qlora_workspace_bytes(d_out, d_in, T, r)
- *          bytes; it must be zero-filled before its first use, and every call
- *          leaves its counter region zero again.
- * T <= 16 runs the weight-streaming (GEMV) kernel; larger T the MFMA GEMM.
+ *          bytes. Its first QLORA_WS_COUNTER_BYTES bytes are u32 counters that
+ *          must be zero before the first use of the workspace; every call leaves
+ *          them zero again. The last four of those words are the handshake of
+ *          the T <= 16 kernel; word 3 becomes nonzero only if a bounded wait in
+ *          that kernel timed out (the call's output is then unspecified).
+ * T <= 16 runs one weight-streaming kernel (the adapter intermediate is formed
+ * by the first workgroups of the same launch); larger T runs the MFMA GEMM.
  */
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A,
                   const uint16_t *B, int32_t r, float alpha, uint16_t *h, float *u_out, void *ws,

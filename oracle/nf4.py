@@ -32,7 +32,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
     (index 7).
   * nearest level: exact comparison in float64 of x = fl32(w/s) against the
     level midpoints, ties to the lower index.
-  * nibble order: element 2m in the low nibble of byte m.
+  * nibble order: codes are packed per run of 8 consecutive weights into one
+    little-endian 32-bit word; byte i (i = 0..3) holds element i in its low
+    nibble and element i+4 in its high nibble. (The pages fix only 4-bit
+    indices; this order lets a byte-select expansion produce the restored
+    values in element order.)
   * double quant: groups of 256 consecutive blocks in flattened row-major order
     (the last group may be short), S_g = max s_k in float32, q2 unsigned 0..255,
     q2 = min(255, rint_half_even(fl32(s_k / S_g) * 256)), q2 = 0 when S_g = 0.
@@ -147,17 +151,17 @@ def nearest_level(xn_f32: np.ndarray, codebook: np.ndarray | None = None) -> np.
 
 
 def pack_codes(q: np.ndarray) -> np.ndarray:
-    """Two 4-bit indices per byte; element 2m in the low nibble of byte m."""
-    q = np.asarray(q, dtype=np.uint8).reshape(-1)
-    return (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+    """Two 4-bit indices per byte: in each run of 8 elements e0..e7, byte i = e_i | e_(i+4) << 4."""
+    q = np.asarray(q, dtype=np.uint8).reshape(-1, 8)
+    return (q[:, 0:4] | (q[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
 
 
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
-    codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
-    q = np.empty(codes.size * 2, dtype=np.uint8)
-    q[0::2] = codes & 0x0F
-    q[1::2] = codes >> 4
-    return q
+    b = np.asarray(codes, dtype=np.uint8).reshape(-1, 4)
+    q = np.empty((b.shape[0], 8), dtype=np.uint8)
+    q[:, 0:4] = b & 0x0F
+    q[:, 4:8] = b >> 4
+    return q.reshape(-1)
 
 
 # ----------------------------------------------------------------------------

@@ -135,6 +135,14 @@ def test_forward_parity(d_out, d_in, r, T):
     assert_close("h", h, h_ref)
     if r > 0:
         assert_close("u", u, u_ref)
+    _assert_workspace_clean()
+
+
+def _assert_workspace_clean():
+    """Every counter and the skinny forward's handshake words are back to zero after a call."""
+    ws = q.workspace("cuda", 1 << 20)
+    counters = ws[:q.COUNTER_BYTES].view(torch.int32)
+    assert int(counters.abs().sum().item()) == 0, "counter / handshake region not reset"
 
 
 @pytest.mark.parametrize("d_out,d_in,r", SHAPES)
@@ -205,6 +213,7 @@ def test_deterministic_reruns(T):
         g = q.qlora_backward(w, d["x"], d["dY"], d["A"], d["B"], case.alpha, u_saved=u)
         torch.cuda.synchronize()
         outs.append([h.clone(), u.clone()] + [t.clone() for t in g])
+    _assert_workspace_clean()
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))

@@ -162,9 +162,11 @@ def _brute_quantize(W):
 
 
 def _brute_pack(q):
+    """Per 8 elements, byte i carries element i (low nibble) and element i+4 (high nibble)."""
     out = []
-    for m in range(len(q) // 2):
-        out.append(q[2 * m] + 16 * q[2 * m + 1])
+    for w in range(len(q) // 8):
+        for i in range(4):
+            out.append(q[8 * w + i] + 16 * q[8 * w + i + 4])
     return out
 
 
@@ -178,6 +180,11 @@ def test_quantize_bruteforce_tiny():
     q = _brute_quantize(W)
     assert list(oracle.unpack_codes(codes)) == q
     assert list(codes) == _brute_pack(q)
+    # word view: nibble k of little-endian word w is element 8w + (k//2) + 4*(k%2)
+    words = codes.view("<u4")
+    for w in range(0, words.size, 7):
+        for k in range(8):
+            assert (int(words[w]) >> (4 * k)) & 15 == q[8 * w + k // 2 + 4 * (k % 2)]
 
 
 def test_quantize_invariants():
