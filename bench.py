@@ -1,25 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the QLoRA frozen-NF4 linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_skinny]
 
 Default workload (LLaMA-7B-shaped projections, the weight-streaming regime):
 4096x4096 and 11008x4096 NF4 + double-quant weights (W ~ N(0, 0.02^2)), LoRA r=64
 alpha=16 (A, B ~ N(0, 0.02^2) bf16), x ~ N(0, 1) bf16 with 1, 4 and 16 tokens.
 One step = the forward h = dequant(W) x + (alpha/r) B A x of both projections at
-all three token counts (6 calls). The quantization happens once before timing,
-as at model load. Every step reads a different copy of the quantized weights
-and adapters (16 copies, ~560 MB) so that HBM, not the 256 MB Infinity Cache,
-serves the weight stream.
+all three token counts (6 calls, each one launch of the weight-streaming kernel).
+Quantization happens once before timing, as at model load.
 
-Printed: one JSON line with the headline metric (weight GB/s: packed codes +
-scale codes + group maxima per second), the roofline of the dominant call
-measured with HIP events on the stream it runs on, and the CPU oracle timed on
-a bounded sample of the same workload.
+Timing. The steps are captured into HIP graphs (a chunk of C steps, replayed),
+so that the host's per-call cost does not leave the GPU idle between 8-15 us
+kernels; HIP events on the replay stream bracket exactly K steps. Every call of
+a chunk reads its own copy of the quantized weight and adapters, so between two
+reads of one copy more than 600 MB of other weights stream by and HBM, not the
+256 MB Infinity Cache, serves the weight stream.
 
-Other workloads (--workload c3 / c4 / c1) time the MFMA GEMM regime (T = 4096
-or 16, forward + backward) for the DESIGN/profiles record; they are not the
-headline line.
+Printed: one JSON line. `value` is the weight GB/s (packed codes + scale codes +
+group maxima per second); `roofline` is the weight-streaming kernel's algorithmic
+bytes per launch over its mean launch duration in the timed region; `cpu_baseline`
+is the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload 13b_4096tok / 65b_layer / linear1024) time the MFMA
+GEMM regime (forward + backward); they are records, not the headline line.
 """
 
 from __future__ import annotations
@@ -38,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer"]
 
 
 def parse():
@@ -45,8 +50,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
-    p.add_argument("--rotate", type=int, default=16, help="independent weight copies cycled through")
+    p.add_argument("--workload", default="llama7b_skinny", choices=WORKLOAD_CHOICES)
+    p.add_argument("--chunk", type=int, default=20, help="steps per captured graph")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -60,29 +66,33 @@ def weight_bytes(d_out, d_in):
     return n // 2 + nb + 4 * ((nb + 255) // 256)
 
 
-def call_bytes(d_out, d_in, r, T, backward=False):
-    """Algorithmic HBM bytes of one call: NF4 weight + adapters + activations in and out."""
-    b = weight_bytes(d_out, d_in) + 2 * r * (d_in + d_out) + 2 * T * (d_in + d_out)
-    if backward:
-        # dY in, dX out, x in again, dA/dB out (f32)
-        b += weight_bytes(d_out, d_in) + 2 * r * (d_in + d_out) + 2 * T * (d_in + d_out) + 2 * T * d_in \
-            + 4 * r * (d_in + d_out)
-    return b
+def fwd_bytes(d_out, d_in, r, T):
+    """Algorithmic HBM bytes of one forward: NF4 weight + adapters + x in + h out."""
+    return weight_bytes(d_out, d_in) + 2 * r * (d_in + d_out) + 2 * T * (d_in + d_out)
 
 
-def call_flops(d_out, d_in, r, T, backward=False):
-    f = 2 * T * d_in * d_out + 2 * T * r * (d_in + d_out)
-    if backward:
-        f += 2 * T * d_in * d_out + 4 * T * r * (d_in + d_out)
-    return f
+def bwd_bytes(d_out, d_in, r, T):
+    """Backward: NF4 weight + adapters + dY, x, u in; dX, dA, dB (f32) out."""
+    return (weight_bytes(d_out, d_in) + 2 * r * (d_in + d_out) + 2 * T * (d_in + d_out) + 2 * T * d_in
+            + 4 * T * r + 4 * r * (d_in + d_out))
+
+
+def fwd_flops(d_out, d_in, r, T):
+    return 2 * T * d_in * d_out + 2 * T * r * (d_in + d_out)
+
+
+def bwd_flops(d_out, d_in, r, T):
+    return 2 * T * d_in * d_out + 4 * T * r * (d_in + d_out)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the layer shards as data parallel across GPUs, which is not built here).", flush=True)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported. The layer shards "
+              "as data parallel (tokens split across GPUs, dA/dB summed); that path is not built.", flush=True)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.chunk < 1:
+        sys.exit("--steps >= 1, --warmup >= 0, --chunk >= 1")
 
     import torch
 
@@ -91,116 +101,128 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
-    cfg = synth.CONFIG_INDEX[args.workload]
+    seed_cfg = synth.WORKLOAD_SEED[args.workload]
+    bw = bool(wl.backward)
+    chunk = min(args.chunk, args.steps)
+    nT = len(wl.tokens)
 
     def dev16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---- inputs: quantize once, replicate the quantized weight for MALL rotation
+    # ---- inputs: quantize once, then replicate the quantized weight so each call of a chunk has its own
     projs = []
     for pi, p in enumerate(wl.projections):
-        W = torch.from_numpy(synth.weight(cfg, pi, p.d_out, p.d_in, wl.weight_dtype)).to(dev)
+        W = torch.from_numpy(synth.weight(seed_cfg, pi, p.d_out, p.d_in, wl.weight_dtype)).to(dev)
         w0 = q.qlora_quantize(W)
         del W
-        (A, A_bits), (B, B_bits) = synth.adapters(cfg, pi, p.d_out, p.d_in, p.r)
-        A0, B0 = dev16(A_bits), dev16(B_bits)
-        ncopy = args.rotate if not wl.backward else 2
-        copies = []
-        for c in range(ncopy):
-            wc = q.NF4Weight(p.d_out, p.d_in, w0.codes.clone(), w0.qscale.clone(), w0.smax.clone())
-            copies.append((wc, A0.clone(), B0.clone()))
-        xs = {T: dev16(synth.tokens(cfg, pi, T, p.d_in)[1]) for T in wl.tokens}
-        dys = {T: dev16(synth.upstream_grad(cfg, pi, T, p.d_out)[1]) for T in wl.tokens} if wl.backward else {}
-        projs.append((p, copies, xs, dys))
+        A0 = B0 = None
+        if p.r > 0:
+            (_, A_bits), (_, B_bits) = synth.adapters(seed_cfg, pi, p.d_out, p.d_in, p.r)
+            A0, B0 = dev16(A_bits), dev16(B_bits)
+        ncopy = chunk * nT if not bw else 2
+        copies = [(w0, A0, B0)]
+        for _ in range(ncopy - 1):
+            copies.append((q.NF4Weight(p.d_out, p.d_in, w0.codes.clone(), w0.qscale.clone(), w0.smax.clone()),
+                           None if A0 is None else A0.clone(), None if B0 is None else B0.clone()))
+        xs = {T: dev16(synth.tokens(seed_cfg, pi, T, p.d_in)[1]) for T in wl.tokens}
+        dys = {T: dev16(synth.upstream_grad(seed_cfg, pi, T, p.d_out)[1]) for T in wl.tokens} if bw else {}
+        outs = {T: torch.empty(T, p.d_out, dtype=torch.bfloat16, device=dev) for T in wl.tokens}
+        grads = {}
+        if bw:
+            for T in wl.tokens:
+                grads[T] = (torch.empty(T, p.d_in, dtype=torch.bfloat16, device=dev),
+                            torch.empty(max(p.r, 1), p.d_in, dtype=torch.float32, device=dev),
+                            torch.empty(p.d_out, max(p.r, 1), dtype=torch.float32, device=dev),
+                            torch.empty(T, max(p.r, 1), dtype=torch.float32, device=dev))
+        projs.append((p, copies, xs, dys, outs, grads))
+    # one workspace large enough for every call, allocated (zeroed) before any capture
+    ws_need = max(q.qlora_workspace_bytes(p.d_out, p.d_in, T, p.r) for p, *_ in projs for T in wl.tokens)
+    q.workspace(dev, ws_need)
     torch.cuda.synchronize()
 
-    calls = []   # (proj, T)
-    for p, copies, xs, dys in projs:
-        for T in wl.tokens:
-            calls.append((p, copies, xs[T], dys.get(T), T))
+    calls = [(p, copies, xs[T], dys.get(T), outs[T], grads.get(T), T, ti)
+             for p, copies, xs, dys, outs, grads in projs for ti, T in enumerate(wl.tokens)]
+
+    def run_call(p, copies, x, dy, h, g, T, ti, k):
+        wc, A, B = copies[k % len(copies)]
+        if not bw:
+            q.qlora_forward(wc, x, A, B, p.alpha, h=h)
+            return
+        dX, dA, dB, u = g
+        ur = u if p.r > 0 else None
+        q.qlora_forward(wc, x, A, B, p.alpha, h=h, u=ur)
+        q.qlora_backward(wc, x, dy, A, B, p.alpha, u_saved=ur, dX=dX, dA=dA if p.r > 0 else None,
+                         dB=dB if p.r > 0 else None)
+
+    def run_steps(s0, n):
+        for s in range(s0, s0 + n):
+            for c in calls:
+                run_call(*c, s * nT + c[-1])
 
     stream = torch.cuda.current_stream(dev)
-    outs = {}
+    for s in range(max(args.warmup, 1)):
+        run_steps(s % chunk, 1)
+    torch.cuda.synchronize()
 
-    def one_call(i, p, copies, x, dy, T, step):
-        wc, A, B = copies[step % len(copies)]
-        key = (i, T)
-        if wl.backward:
-            h, u = q.qlora_forward(wc, x, A, B, p.alpha, save_u=True, h=outs.get(key))
-            outs[key] = h
-            q.qlora_backward(wc, x, dy, A, B, p.alpha, u_saved=u)
+    # ---- graphs: one of `chunk` steps, and one of the remainder
+    graphs = {}
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)  # default priority
+        for n in sorted({chunk, args.steps % chunk} - {0}):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                run_steps(0, n)
+            graphs[n] = g
+        torch.cuda.synchronize()
+        for n, g in graphs.items():       # one untimed replay of each
+            g.replay()
+        torch.cuda.synchronize()
+
+    def timed(K):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        if graphs:
+            for _ in range(K // chunk):
+                graphs[chunk].replay()
+            if K % chunk:
+                graphs[K % chunk].replay()
         else:
-            h, _ = q.qlora_forward(wc, x, A, B, p.alpha, h=outs.get(key))
-            outs[key] = h
+            run_steps(0, K)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
 
-    def step(s, events=None):
-        for i, (p, copies, x, dy, T) in enumerate(calls):
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                one_call(i, p, copies, x, dy, T, s)
-                e1.record(stream)
-                events.append((i, e0, e1))
-            else:
-                one_call(i, p, copies, x, dy, T, s)
+    ms_total = timed(args.steps)
+    ms_step = ms_total / args.steps
 
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-
-    # timed region: whole steps (no per-call events) ...
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for s in range(args.steps):
-        step(args.warmup + s)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-
-    # ... and the same steps again with HIP events around every call on its stream
-    events = []
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        step(args.warmup + s, events)
-    torch.cuda.synchronize()
-    per_call_ms = [[] for _ in calls]
-    for i, e0, e1 in events:
-        per_call_ms[i].append(e0.elapsed_time(e1))
-
-    bw = bool(wl.backward)
-    wbytes_step = sum(weight_bytes(p.d_out, p.d_in) * (2 if bw else 1) for p, _, _, _, _ in calls)
-    bytes_step = sum(call_bytes(p.d_out, p.d_in, p.r, T, bw) for p, _, _, _, T in calls)
-    flops_step = sum(call_flops(p.d_out, p.d_in, p.r, T, bw) for p, _, _, _, T in calls)
+    fb = sum(fwd_bytes(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls)
+    ff = sum(fwd_flops(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls)
+    bb = sum(bwd_bytes(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls) if bw else 0
+    bf = sum(bwd_flops(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls) if bw else 0
+    wbytes_step = sum(weight_bytes(p.d_out, p.d_in) for p, *_ in calls) * (2 if bw else 1)
     wgbs = wbytes_step / (ms_step * 1e-3) / 1e9
-    tflops = flops_step / (ms_step * 1e-3) / 1e12
-
-    call_rows = []
-    for i, (p, _, _, _, T) in enumerate(calls):
-        ms = float(np.mean(per_call_ms[i]))
-        b = call_bytes(p.d_out, p.d_in, p.r, T, bw)
-        f = call_flops(p.d_out, p.d_in, p.r, T, bw)
-        call_rows.append({"proj": f"{p.d_out}x{p.d_in}", "T": T, "r": p.r, "us": round(ms * 1e3, 2),
-                          "GBs": round(b / (ms * 1e-3) / 1e9, 1), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 2)})
+    tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
 
     if not bw:
-        # memory-bound regime: dominant call = the forward that moves the most bytes
-        tot_b = sum(call_bytes(p.d_out, p.d_in, p.r, T) for p, _, _, _, T in calls)
-        tot_ms = sum(float(np.mean(per_call_ms[i])) for i in range(len(calls)))
-        achieved = tot_b / (tot_ms * 1e-3) / 1e9
+        # every call is one launch of the weight-streaming kernel (T <= 16): its mean launch duration over
+        # the timed region is the region's length over the launches in it
+        launches = args.steps * len(calls)
+        us_launch = ms_total * 1e3 / launches
+        achieved = (fb / len(calls)) / (us_launch * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "qlora_forward T<=16 (k_lora_small + k_gemv_fwd), mean over the 6 calls",
-                "per_call": call_rows}
+                "kernel": "k_gemv_fwd (qlora_forward, T <= 16)",
+                "bytes_per_launch": round(fb / len(calls)), "us_per_launch": round(us_launch, 3),
+                "launches": launches}
     else:
-        tot_f = sum(call_flops(p.d_out, p.d_in, p.r, T, True) for p, _, _, _, T in calls)
-        tot_ms = sum(float(np.mean(per_call_ms[i])) for i in range(len(calls)))
-        achieved = tot_f / (tot_ms * 1e-3) / 1e12
+        achieved = (ff + bf) / (ms_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "qlora_forward + qlora_backward per projection", "per_call": call_rows}
+                "kernel": "whole forward + backward step (all kernels)"}
+
+    per_call = per_call_times(torch, dev, calls, run_call, chunk) if not args.no_graph else []
 
     if args.copy_calibration:
         a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
@@ -211,8 +233,8 @@ def main():
         del a, b
 
     cpu = None
-    if not args.no_cpu_baseline and not wl.backward:
-        cpu = cpu_baseline(args, wl, cfg, calls, wbytes_step, bytes_step)
+    if not args.no_cpu_baseline and not bw:
+        cpu = cpu_baseline(args, wl, seed_cfg, wbytes_step)
 
     line = {
         "metric": METRIC,
@@ -229,16 +251,49 @@ def main():
         "data": "synthetic (seeded N(0,0.02^2) weights and adapters, N(0,1) tokens)",
         "config": {"workload": wl.description, "projections": [f"{p.d_out}x{p.d_in}" for p in wl.projections],
                    "tokens": list(wl.tokens), "lora_r": wl.projections[0].r, "lora_alpha": wl.projections[0].alpha,
-                   "backward": bw, "weight_copies_rotated": len(projs[0][1])},
+                   "backward": bw, "graph_steps": chunk if graphs else 0,
+                   "weight_copies_per_projection": len(projs[0][1])},
         "tflops": round(tflops, 3),
-        "total_GBs": round(bytes_step / (ms_step * 1e-3) / 1e9, 1),
+        "total_GBs": round((fb + bb) / (ms_step * 1e-3) / 1e9, 1),
         "roofline": roof,
+        "per_call": per_call,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(args, wl, cfg, calls, wbytes_step, bytes_step):
+def per_call_times(torch, dev, calls, run_call, chunk):
+    """Each call shape alone: a graph of `chunk`*3 launches of it over rotating copies, replayed 5 times."""
+    rows = []
+    side = torch.cuda.Stream(dev)
+    stream = torch.cuda.current_stream(dev)
+    for c in calls:
+        p, copies, x, dy, h, g, T, ti = c
+        n = min(len(copies), 3 * chunk)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            for k in range(n):
+                run_call(p, copies, x, dy, h, g, T, ti, k)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(5):
+            gr.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (5 * n)
+        b = fwd_bytes(p.d_out, p.d_in, p.r, T)
+        rows.append({"proj": f"{p.d_out}x{p.d_in}", "T": T, "r": p.r, "us": round(us, 2),
+                     "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                     "weight_GBs": round(weight_bytes(p.d_out, p.d_in) / (us * 1e-6) / 1e9, 1)})
+        del gr
+    return rows
+
+
+def cpu_baseline(args, wl, seed_cfg, wbytes_step):
     """The CPU oracle timed on a bounded sample of the same workload (host cores of this machine)."""
     import oracle
     from bit_quantized_finetuning_amd import synth
@@ -251,10 +306,10 @@ def cpu_baseline(args, wl, cfg, calls, wbytes_step, bytes_step):
     # Per projection: quantized once (not timed, as on the GPU); timed: restore + forward for every T.
     prepared = []
     for pi, p in enumerate(wl.projections):
-        W = synth.weight(cfg, pi, p.d_out, p.d_in, wl.weight_dtype)
+        W = synth.weight(seed_cfg, pi, p.d_out, p.d_in, wl.weight_dtype)
         codes, q2, S = oracle.quantize(W)
-        (A, _), (B, _) = synth.adapters(cfg, pi, p.d_out, p.d_in, p.r)
-        xs = {T: synth.tokens(cfg, pi, T, p.d_in)[0] for T in wl.tokens}
+        (A, _), (B, _) = synth.adapters(seed_cfg, pi, p.d_out, p.d_in, p.r)
+        xs = {T: synth.tokens(seed_cfg, pi, T, p.d_in)[0] for T in wl.tokens}
         prepared.append((p, codes, q2, S, A, B, xs))
     done_steps = 0
     t_start = time.perf_counter()
@@ -265,7 +320,7 @@ def cpu_baseline(args, wl, cfg, calls, wbytes_step, bytes_step):
                 oracle.lora_forward(wb, xs[T], A, B, p.alpha, p.r)
         done_steps += 1
         el = time.perf_counter() - t_start
-        if el >= args.cpu_seconds or wl.backward:
+        if el >= args.cpu_seconds:
             break
     sec_step = el / done_steps
     return {"value": round(wbytes_step / sec_step / 1e9, 4), "unit": "GB/s (NF4 weight bytes per second)",

@@ -196,8 +196,11 @@ def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:
 
 
 def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
-                  save_u: bool = False, h: torch.Tensor | None = None):
-    """h = x W_hat^T + (alpha/r) (x A^T) B^T. Returns (h, u) with u float32 [T, r] if save_u else None."""
+                  save_u: bool = False, h: torch.Tensor | None = None, u: torch.Tensor | None = None):
+    """h = x W_hat^T + (alpha/r) (x A^T) B^T. Returns (h, u); u is float32 [T, r] when save_u or given, else None.
+
+    h and u may be passed in (preallocated outputs); otherwise they are allocated here.
+    """
     x = _bits(x)
     T = x.shape[0]
     r = 0 if A is None else A.shape[0]
@@ -205,7 +208,8 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
         _bits(A), _bits(B)
     if h is None:
         h = torch.empty(T, w.d_out, dtype=torch.bfloat16, device=x.device)
-    u = torch.empty(T, r, dtype=torch.float32, device=x.device) if (save_u and r > 0) else None
+    if u is None and save_u and r > 0:
+        u = torch.empty(T, r, dtype=torch.float32, device=x.device)
     nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
     ws = workspace(x.device, nbytes)
     cw = w._c()
@@ -216,15 +220,22 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
 
 def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor | None,
                    B: torch.Tensor | None, alpha: float, u_saved: torch.Tensor | None = None,
-                   need_dx: bool = True, need_dA: bool = True, need_dB: bool = True):
-    """Returns (dX bf16 [T, d_in] | None, dA f32 [r, d_in] | None, dB f32 [d_out, r] | None)."""
+                   need_dx: bool = True, need_dA: bool = True, need_dB: bool = True,
+                   dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None):
+    """Returns (dX bf16 [T, d_in] | None, dA f32 [r, d_in] | None, dB f32 [d_out, r] | None).
+
+    Outputs passed in are written in place (and count as needed); the others are allocated when needed.
+    """
     dY = _bits(dY)
     T = dY.shape[0]
     r = 0 if A is None else A.shape[0]
     dev = dY.device
-    dX = torch.empty(T, w.d_in, dtype=torch.bfloat16, device=dev) if need_dx else None
-    dA = torch.empty(r, w.d_in, dtype=torch.float32, device=dev) if (need_dA and r > 0) else None
-    dB = torch.empty(w.d_out, r, dtype=torch.float32, device=dev) if (need_dB and r > 0) else None
+    if dX is None and need_dx:
+        dX = torch.empty(T, w.d_in, dtype=torch.bfloat16, device=dev)
+    if dA is None and need_dA and r > 0:
+        dA = torch.empty(r, w.d_in, dtype=torch.float32, device=dev)
+    if dB is None and need_dB and r > 0:
+        dB = torch.empty(w.d_out, r, dtype=torch.float32, device=dev)
     nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
     ws = workspace(dev, nbytes)
     cw = w._c()

@@ -45,17 +45,17 @@ class Workload:
 
 
 WORKLOADS = {
-    "c1": Workload("c1", "single linear 1024x1024, LoRA r=8 alpha=16, 16 tokens, fwd+bwd",
+    "linear1024": Workload("linear1024", "single linear 1024x1024, LoRA r=8 alpha=16, 16 tokens, fwd+bwd",
                    (Projection("linear", 1024, 1024, 8, 16.0),), (16,), True, "f32"),
-    "c2": Workload("c2", "LLaMA-7B projections 4096x4096 and 11008x4096, LoRA r=64 alpha=16, "
+    "llama7b_skinny": Workload("llama7b_skinny", "LLaMA-7B projections 4096x4096 and 11008x4096, LoRA r=64 alpha=16, "
                    "1/4/16 tokens, forward",
                    (Projection("q_proj", 4096, 4096, 64, 16.0),
                     Projection("up_proj", 11008, 4096, 64, 16.0)), (1, 4, 16), False, "f32"),
-    "c3": Workload("c3", "13B projections 5120x5120 and 13824x5120, LoRA r=64 alpha=16, "
+    "13b_4096tok": Workload("13b_4096tok", "13B projections 5120x5120 and 13824x5120, LoRA r=64 alpha=16, "
                    "4096 tokens (8x512), fwd+bwd",
                    (Projection("q_proj", 5120, 5120, 64, 16.0),
                     Projection("up_proj", 13824, 5120, 64, 16.0)), (4096,), True, "f32"),
-    "c4": Workload("c4", "65B decoder layer, hidden 8192, MLP 22016, LoRA r=64 alpha=16 on all "
+    "65b_layer": Workload("65b_layer", "65B decoder layer, hidden 8192, MLP 22016, LoRA r=64 alpha=16 on all "
                    "projections, 4096 tokens, fwd+bwd",
                    (Projection("q_proj", 8192, 8192, 64, 16.0),
                     Projection("k_proj", 8192, 8192, 64, 16.0),
@@ -65,7 +65,7 @@ WORKLOADS = {
                     Projection("up_proj", 22016, 8192, 64, 16.0),
                     Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
     # 14B-style stack: k/v are 1024x5120 (8 KV heads x 128); LoRA r=8 on q and v only.
-    "c5": Workload("c5", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 alpha=16 "
+    "14b_stack": Workload("14b_stack", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 alpha=16 "
                    "on q/v, 2048 tokens, fwd+bwd",
                    (Projection("q_proj", 5120, 5120, 8, 16.0),
                     Projection("k_proj", 1024, 5120, 0, 16.0),
@@ -75,7 +75,8 @@ WORKLOADS = {
                     Projection("up_proj", 17408, 5120, 0, 16.0),
                     Projection("down_proj", 5120, 17408, 0, 16.0)), (2048,), True, "bf16", layers=40),
 }
-CONFIG_INDEX = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+# second component of every RNG seed list, one per workload
+WORKLOAD_SEED = {"linear1024": 1, "llama7b_skinny": 2, "13b_4096tok": 3, "65b_layer": 4, "14b_stack": 5}
 
 
 def rng(config: int, projection: int, tensor: int, seed: int = 0) -> np.random.Generator:

@@ -145,7 +145,7 @@ def test_lora_parameter_counts_from_pages():
     assert round(2 * d * r / (d * d), 3) == g["lora_fraction_d4096_r8"]["value"]
     # GPU-fit page: Qwen3-14B with LoRA r=8 on q_proj, v_proj has 5.24 M trainable parameters;
     # the 14B-style stack workload (40 layers, q 5120x5120, v 1024x5120) reproduces it.
-    wl = synth.WORKLOADS["c5"]
+    wl = synth.WORKLOADS["14b_stack"]
     n = 0
     for p in wl.projections:
         if p.r:
