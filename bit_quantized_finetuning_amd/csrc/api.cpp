@@ -67,6 +67,19 @@ const Nf4Consts &consts() {
   return t.c;
 }
 
+// The restore kernels carry the levels as literals; they must equal the derived table.
+bool literals_match() {
+  static const bool ok = [] {
+    for (int j = 0; j < 16; ++j) {
+      uint32_t b;
+      std::memcpy(&b, &consts().code[j], 4);
+      if (b != kNf4CodeBits[j]) return false;
+    }
+    return true;
+  }();
+  return ok;
+}
+
 // Per-tile buffer ranges stay below 2^31 bytes with these bounds.
 constexpr int64_t kMaxDim = (int64_t)1 << 20;
 constexpr int64_t kMaxTokens = (int64_t)1 << 24;
@@ -77,6 +90,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int validate_weight(const qlora_nf4_weight *W) {
+  if (!literals_match()) return QLORA_ERR_INTERNAL;
   if (!W || !W->codes || !W->qscale || !W->smax) return QLORA_ERR_NULL;
   if (W->d_out < 1 || W->d_in < QLORA_BLOCK || W->d_in % QLORA_BLOCK != 0 || W->d_out % 16 != 0)
     return QLORA_ERR_SHAPE;
@@ -110,7 +124,7 @@ Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
   L.sx = off;
   off = align256(off + (size_t)T16 * rp * 2);
   L.su32 = off;
-  off = align256(off + (size_t)gemv_ksplit(d_in) * 16 * rp * 4);
+  off = align256(off + (size_t)4 * 16 * rp * 8);  // tagged float32 partials of u (4 K slices)
   L.u = off;
   off = align256(off + (size_t)T * r * 4);
   L.v = off;
@@ -157,6 +171,7 @@ const char *qlora_status_string(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_DTYPE: return "unknown dtype";
     case QLORA_ERR_HIP: return "HIP launch failed";
+    case QLORA_ERR_INTERNAL: return "internal: the kernels' NF4 levels differ from the derived table";
     default: return "unknown status";
   }
 }
@@ -214,9 +229,9 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   const Nf4Consts &c = consts();
   const int rp = rank_pad(r);
   const float sc = r > 0 ? alpha / (float)r : 0.f;
-  if (T <= 16)
+  if (gemv_supported(d_out, d_in, T))
     return hip_status(launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, A, B, r, rp, sc, h, u_out,
-                                      at<float>(ws, L.su32), at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4), c,
+                                      at<uint64_t>(ws, L.su32), at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4),
                                       stream));
   uint16_t *su = at<uint16_t>(ws, L.sx);
   float *partial = at<float>(ws, L.partial);

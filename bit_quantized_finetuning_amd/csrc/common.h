@@ -21,14 +21,22 @@ constexpr int kGroup = 256;
 // Split reductions count arriving workgroups per output tile in a fixed region
 // at the start of the workspace (zero before first use, left zero by every
 // kernel). A kernel whose tile count exceeds kMaxTileCounters runs without a
-// split. The last kSyncWords words of the region are the skinny forward's
-// producer/consumer handshake.
+// split. The last kSyncWords words of the region are reserved for the skinny
+// forward; the last of them is set if one of its bounded waits timed out.
 constexpr int64_t kMaxCounters = 16384;
 constexpr int64_t kSyncWords = 4;
 constexpr int64_t kMaxTileCounters = kMaxCounters - kSyncWords;
 
-// Codebook and decision thresholds, passed to kernels by value (kernel arguments
-// live in SGPRs; they are only ever indexed with compile-time constants).
+// The 16 NF4 levels as float32 bit patterns, ascending. Kernels that build
+// restore tables take them as literal operands (no registers held across the
+// loop). The host derives the same table from normal quantiles and checks it
+// against this one, bit for bit, before it launches anything.
+constexpr uint32_t kNf4CodeBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du, 0xbdba7869u, 0x00000000u,
+    0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+// Codebook and decision thresholds, passed by value to the kernels that index
+// them (kernel arguments live in SGPRs; only compile-time indices are used).
 struct Nf4Consts {
   float code[16];
   float thr[15];
@@ -73,10 +81,18 @@ struct Nf4Planes {
   uint32_t hi[4];
 };
 
-__device__ __forceinline__ Nf4Planes make_planes(const Nf4Consts &c, float sh) {
+__device__ __forceinline__ float code_times(int j, float sh) {
+  // fl32(c[j] * sh); c[0] = -1, c[7] = 0 and c[15] = 1 need no multiply
+  if (j == 0) return -sh;
+  if (j == 7) return 0.f;
+  if (j == 15) return sh;
+  return __uint_as_float(kNf4CodeBits[j]) * sh;
+}
+
+__device__ __forceinline__ Nf4Planes make_planes(float sh) {
   uint32_t p[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) p[k] = pack_bf16x2(c.code[2 * k] * sh, c.code[2 * k + 1] * sh);
+  for (int k = 0; k < 8; ++k) p[k] = pack_bf16x2(code_times(2 * k, sh), code_times(2 * k + 1, sh));
   Nf4Planes t;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -184,6 +200,34 @@ __device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
 __device__ __forceinline__ uint32_t add_dev_u32(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A 32-bit name of the running launch: the dispatch id (the queue's packet
+// counter, which advances for every launch, graph replays included) mixed with
+// the queue address; never zero. Read from registers set up at wave launch.
+extern "C" __device__ uint64_t qlora_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+__device__ __forceinline__ uint32_t launch_tag() {
+  const uint64_t d = qlora_llvm_dispatch_id();
+  const uint64_t q = (uint64_t)(uintptr_t)__builtin_amdgcn_queue_ptr();
+  const uint32_t t = (uint32_t)d ^ (uint32_t)(q >> 8) ^ (uint32_t)(q >> 40);
+  return t ? t : 1u;
+}
+
+// 64-bit device-scope store / load: naturally aligned, so a reader sees either
+// the old or the new 8 bytes, never a mix (a value and its tag travel together).
+__device__ __forceinline__ void st_dev_u64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Workgroup barrier that orders LDS accesses only. A plain __syncthreads() also
+// waits for every outstanding global load and store of each wave, which would
+// drain prefetches and device-scope publishes at every barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(const uint8_t *__restrict__ co
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
     for (int i = 0; i < 8; ++i) st16(as + (xr_ + 32 * i) * kAP + xc, xa[i]);
-    const Nf4Planes t = make_planes(c, restore_scale(q2, S));
+    const Nf4Planes t = make_planes(restore_scale(q2, S));
     uint16_t *bs = Bs + buf * kBN * kAP + tid * kAP;
 #pragma unroll
     for (int m = 0; m < 4; ++m) st16(bs + 8 * m, expand8(t, cw0[m]));
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint8_t *__restrict__ cod
     uint16_t *as = As + buf * kBM * kAP;
 #pragma unroll
     for (int i = 0; i < 8; ++i) st16(as + (xr_ + 32 * i) * kAP + xc, xa[i]);
-    const Nf4Planes t = make_planes(c, restore_scale(q2, S));
+    const Nf4Planes t = make_planes(restore_scale(q2, S));
     uint16_t *bt = Bt + buf * kBK * kBTP + wo * kBTP + wb * 64;
 #pragma unroll
     for (int m = 0; m < 4; ++m) st16(bt + 8 * m, expand8(t, cw0[m]));

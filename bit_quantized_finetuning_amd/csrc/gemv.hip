@@ -4,10 +4,10 @@
 // restored frozen base plus the adapter term, s = alpha/r).
 //
 // Every weight is used by at most 16 tokens, so the kernel is bound by the
-// packed-weight stream (0.516 bytes per weight) and by the VALU work of the
-// restore (~3.7 instructions per weight). Calls of this size are also dominated
-// by launch, ramp and memory latency, so the design issues as many loads as
-// possible up front and keeps the per-wave fixed work small.
+// packed-weight stream (0.516 bytes per weight), by the VALU work of the
+// restore (about 3.5 instructions per weight) and, at these sizes, by launch
+// and memory latency. The design therefore issues its loads early, in the
+// order they are needed, and keeps the per-item bookkeeping out of the VALU.
 //
 // One grid of G workgroups of kW waves, one per CU (G = min(row tiles, CUs)):
 //   * workgroup c streams row tiles c, c+G, c+2G, ... of 16 output rows. The
@@ -15,32 +15,49 @@
 //     64-weight block (two 16-byte code loads), builds that block's restore
 //     table once and feeds 8 v_mfma_f32_16x16x32_bf16 (tokens on M, padded to
 //     16; rows on N). Each wave prefetches its next (row tile, segment) item
-//     while computing the current one (two register stages in ping-pong). x is
-//     staged once per workgroup in LDS when it fits (T x d_in bf16 <= 136 KB)
-//     and is otherwise read per segment from global memory. At the end of a row
-//     tile the waves reduce through LDS and write h; wave 0 first adds s*u B^T
-//     as r_pad more K columns.
-//   * the first P workgroups also produce the adapter intermediate at their
-//     start: job (j, ks) computes columns 16j..16j+15 of u = x A^T over the
-//     ks-th of ksp K slices, publishes the partial with device-scope stores and
-//     bumps a counter; the last job raises a ready flag.
-//   * s*u is formed once per workgroup: wave 0 issues the ready-flag load before
-//     streaming; at the first row-tile end every thread sums its entries over
-//     the ksp partials in slice order (deterministic) into LDS. The last
-//     workgroup through resets the flag.
-// The grid never exceeds one residency (one workgroup per CU), producer jobs
-// come before any wait, and the spin is bounded anyway (timeout -> status word,
-// never a hang). All per-lane offsets are 32-bit against buffer ranges rebased
-// per row tile.
+//     while computing the current one (two register stages in ping-pong).
+//   * x is staged in LDS when it fits (T x d_in bf16 <= 136 KB), each wave
+//     staging just the segments it computes with, so no workgroup barrier
+//     stands before the first item; the segment order is rotated per workgroup
+//     so that the CUs, which all read all of x, spread over the L2 channels.
+//     Otherwise x is read per segment from global memory. Loads go out in the
+//     order they are needed (they complete in issue order).
+//   * the last P = 4 r_pad/16 workgroups (those with the fewest row tiles)
+//     also produce the adapter intermediate: producer (j, ks) forms the
+//     partial of columns 16j..16j+15 of u = x A^T over the ks-th quarter of K
+//     (a single CU streams only a few tens of GB/s, so the A reads are
+//     spread). Its A and x operands are its first loads and the job runs
+//     before anything else, so each float32 partial is published early,
+//     together with a tag in one 64-bit device-scope store. No counter or flag
+//     sits between producer and reader.
+//   * the tag names the launch: the dispatch id of the kernel (a per-queue
+//     packet counter, new for every launch and every graph replay) mixed with
+//     the queue's address. Every workgroup has it in registers from the start,
+//     so nothing is read from memory or counted to agree on it. An entry left
+//     by an earlier launch could only match after 2^32 launches on one queue,
+//     or, across queues, with probability 2^-32 per change of queue.
+//   * s*u is read once per workgroup: the loads go out before the last item of
+//     the first row tile, and at that tile's end the entries are checked (and
+//     re-read until their tags match, with a bounded wait), the four partials
+//     summed in slice order and bf16(s*u) put in LDS; wave 0 then adds s*u B^T
+//     as r_pad more K columns. Workgroup 0 writes float32 u for the backward.
+//   * at the end of a row tile the waves reduce through LDS and write h.
+// The grid never exceeds one residency, producers never wait for anyone, and
+// the one wait is bounded (timeout -> status word, never a hang). Buffer
+// descriptors cover whole tensors (the launcher requires the packed codes to
+// stay below 2^31 bytes); per-lane offsets are 32-bit and an out-of-range lane
+// reads zero.
 #include "kernels.h"
 
 namespace qlora {
 
-constexpr int kSpinLimit = 1 << 21;  // ~60 ms of s_sleep; only a safety net
-constexpr int kMaxKsp = 8;           // K slices per adapter column tile
+constexpr int kSpinLimit = 1 << 20;  // bounded wait; only a safety net
 constexpr int kMaxRpad = 256;
 constexpr int kXPad = 8;             // bf16 of padding per staged x row (rows 4 banks apart)
 constexpr int kXLdsBytes = 136 * 1024;
+constexpr int kABatch = 8;           // producer K steps (of 32) per wave per batch
+constexpr int kKsp = 4;              // K slices of the adapter intermediate (one producer each)
+constexpr int kPairsAhead = 2;       // s*u entries per thread read ahead (x kKsp partials)
 
 struct GemvCodes {
   u32x4 c0, c1;  // 32 bytes of codes = one 64-weight block
@@ -55,144 +72,213 @@ template <int kW, bool kXL>
 __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ qscale, const float *__restrict__ smax,
     int d_out, int d_in, const uint16_t *__restrict__ x, int T, const uint16_t *__restrict__ A,
-    const uint16_t *__restrict__ B, int r, int r_pad, int ksp, float scale, uint16_t *__restrict__ h,
-    float *__restrict__ u_out, float *__restrict__ upart, uint32_t *__restrict__ sync, Nf4Consts c) {
+    const uint16_t *__restrict__ B, int r, int r_pad, float scale, uint16_t *__restrict__ h,
+    float *__restrict__ u_out, uint64_t *__restrict__ uex, uint32_t *__restrict__ sync) {
+  // All kernel arguments in one scalar-memory round trip (left alone, the
+  // compiler fetches them in dependent batches at first use).
+  asm volatile("; kernel arguments" ::"s"(codes), "s"(qscale), "s"(smax), "s"(d_out), "s"(d_in), "s"(x), "s"(T),
+               "s"(A), "s"(B), "s"(r), "s"(r_pad), "s"(scale), "s"(h), "s"(u_out), "s"(uex), "s"(sync),
+               "s"(gridDim.x));
   constexpr int kThreads = 64 * kW;
+  constexpr int kPollPer = 16 * kMaxRpad / 2 / kThreads;  // tagged pairs per thread, at most
   extern __shared__ __attribute__((aligned(16))) uint16_t x_l[];  // [T][d_in + kXPad] when kXL
   __shared__ float red[kW][256];
   __shared__ __attribute__((aligned(16))) uint16_t su_l[16 * kMaxRpad];
+  __shared__ int poll_bad[2][kW];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int li = lane & 15, g = lane >> 4;
-  const int P = r > 0 ? (r_pad / 16) * ksp : 0;
+  const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
   const int KB = d_in / kBlock;
   const int cid = blockIdx.x, G = gridDim.x;
-  const rsrc_t xr = make_rsrc(x, (int64_t)T * d_in * 2);
   const int xpitch = d_in + kXPad;
-
-  // ---------------- items: (row tile k, segment s) of this wave ----------------
   const int RT = (d_out + 15) / 16;
   const int nrt = cid < RT ? (RT - cid + G - 1) / G : 0;
   const int NS = (KB + 3) / 4;
-  const int mseg = NS > wave ? (NS - wave + kW - 1) / kW : 0;  // my segments per row tile
-  const uint32_t lane_code = (uint32_t)(li * (d_in / 2) + g * (kBlock / 2));
-  const uint32_t lane_q2 = (uint32_t)(li * KB + g);
-  const int64_t ngroups = ((int64_t)d_out * KB + kGroup - 1) / kGroup;
+  // Segments seg = wv + kW s of every row tile belong to wave slot wv; the slot
+  // is rotated per workgroup so that at any moment different workgroups read
+  // different parts of x (every CU reads all of x).
+  const int wv = (wave + cid) % kW;
+  const int mseg = NS > wv ? (NS - wv + kW - 1) / kW : 0;  // my segments per row tile
+  const int nblocks = d_out * KB;
+  const rsrc_t cr = make_rsrc(codes, (int64_t)nblocks * (kBlock / 2));
+  const rsrc_t qr = make_rsrc(qscale, nblocks);
+  const rsrc_t sr = make_rsrc(smax, (int64_t)((nblocks + kGroup - 1) / kGroup) * 4);
+  const rsrc_t xr = make_rsrc(x, (int64_t)T * d_in * 2);
 
+  // Item (row tile k, segment s): lane (li, g) takes block g of the segment in
+  // row 16 (c + kG) + li. Rows past d_out (ragged tile, k >= nrt) read zeros.
   auto load_codes = [&](int k, int s, GemvCodes &st) {
-    const int row0 = (cid + k * G) * 16;
-    const bool krow = k < nrt;
-    const int rows = krow ? (d_out - row0 < 16 ? d_out - row0 : 16) : 0;
-    const int kb0 = 4 * (wave + kW * s);  // first block of the segment
-    const bool ok = kb0 + g < KB && li < rows;
-    const int64_t rb = krow ? row0 : 0;
-    const rsrc_t cr = make_rsrc(codes + rb * (d_in / 2), (int64_t)rows * (d_in / 2));
-    const uint32_t coff = ok ? lane_code + (uint32_t)kb0 * (kBlock / 2) : kOOB;
-    st.c0 = bld16(cr, coff);
-    st.c1 = bld16(cr, coff + 16);
-    const rsrc_t qr = make_rsrc(qscale + rb * KB, (int64_t)rows * KB);
-    st.q2 = bld8(qr, ok ? lane_q2 + (uint32_t)kb0 : kOOB);
-    // group maximum of block (row0 + li, kb0 + g), range rebased at the row tile's first group
-    const int64_t blk0 = rb * KB;
-    const rsrc_t sr = make_rsrc(smax + (blk0 >> 8), (ngroups - (blk0 >> 8)) * 4);
-    const uint32_t rel = (uint32_t)(blk0 & (kGroup - 1)) + (uint32_t)(li * KB) + (uint32_t)(kb0 + g);
-    st.S = __uint_as_float(bld32(sr, ok ? (rel >> 8) * 4 : kOOB));
+    const int row = (cid + k * G) * 16 + li;
+    const int kb = 4 * (wv + kW * s) + g;
+    const bool ok = row < d_out && kb < KB;
+    const uint32_t blk = (uint32_t)row * (uint32_t)KB + (uint32_t)kb;
+    st.c0 = bld16(cr, ok ? blk * 32u : kOOB);
+    st.c1 = bld16(cr, ok ? blk * 32u + 16u : kOOB);
+    st.q2 = bld8(qr, ok ? blk : kOOB);
+    st.S = __uint_as_float(bld32(sr, ok ? (blk >> 8) * 4u : kOOB));
   };
   auto load_x = [&](int s, GemvX &st) {
-    const int kbl = 4 * (wave + kW * s) + g;
-    const uint32_t xoff = kbl < KB ? (uint32_t)((li * d_in + kbl * kBlock) * 2) : kOOB;
+    const int kb = 4 * (wv + kW * s) + g;
+    const uint32_t xoff = kb < KB ? (uint32_t)((li * d_in + kb * kBlock) * 2) : kOOB;
 #pragma unroll
     for (int m = 0; m < 8; ++m) st.x[m] = bld16(xr, xoff + 16 * m);
   };
 
-  // ---------------- first loads, handshake read ----------------
+  // ---------------- loads in the order they are needed ----------------
+  // Loads complete in issue order, so everything a step waits for goes out
+  // before the loads it does not need yet.
+
+  // producer (j, ks): A rows 16j..16j+15 over K slice ks (steps of 32 split
+  // over the waves). A CU streams only a few tens of GB/s on its own, so the
+  // A reads are spread over kKsp producers per column tile. Producers are the
+  // last P workgroups, which hold the fewest row tiles.
+  const int pid = cid - (G - P);
+  const bool producer = P > 0 && pid >= 0;
+  const int pj = producer ? pid / kKsp : 0, pks = producer ? pid % kKsp : 0;
+  const int nk32 = d_in / 32;
+  const int k32b = producer ? nk32 * pks / kKsp : 0, k32e = producer ? nk32 * (pks + 1) / kKsp : 0;
+  const int arows = producer ? (r - 16 * pj < 16 ? r - 16 * pj : 16) : 0;
+  const rsrc_t ar = make_rsrc(A + (producer ? (int64_t)16 * pj * d_in : 0), (int64_t)arows * d_in * 2);
+  u32x4 ap[kABatch], xp[kABatch];
+  auto a_issue = [&](int b) {
+#pragma unroll
+    for (int s = 0; s < kABatch; ++s) {
+      const int k32 = k32b + wave + kW * (kABatch * b + s);
+      const uint32_t off = k32 < k32e ? (uint32_t)((li * d_in + k32 * 32 + 8 * g) * 2) : kOOB;
+      ap[s] = bld16(ar, off);
+      xp[s] = bld16(xr, off);  // x row li has the same offsets as A row li
+    }
+  };
+
+  // x staging, per wave: only the 256-column segments this wave computes with
+  // (a producer workgroup stages all of x the same way, then joins up). Load i
+  // of a segment covers tokens 2i, 2i+1: lane l takes token 2i + l/32,
+  // columns 8 (l % 32) .. + 8. Two segments go per batch.
+  constexpr int kXSeg = 2;
+  u32x4 xs[kXSeg][8];
+  auto x_addr = [&](int j, int i, int &t, int &col) {
+    t = 2 * i + (lane >> 5);
+    col = 256 * (wv + kW * j) + 8 * (lane & 31);
+    return j < mseg && t < T && col < d_in;
+  };
+  auto x_issue = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kXSeg; ++jj)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int t, col;
+        const bool ok = x_addr(j0 + jj, i, t, col);
+        xs[jj][i] = bld16(xr, ok ? (uint32_t)((t * d_in + col) * 2) : kOOB);
+      }
+  };
+  auto x_store = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kXSeg; ++jj)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int t, col;
+        if (x_addr(j0 + jj, i, t, col)) st16(x_l + t * xpitch + col, xs[jj][i]);
+      }
+  };
+  // A producer's own operands go out first: its job needs nothing else.
+  if (producer) a_issue(0);
+  if (kXL && mseg > 0) x_issue(0);
+
   GemvCodes ca, cb;
   GemvX xa, xb;
   if (mseg > 0) {
     load_codes(0, 0, ca);
     if (!kXL) load_x(0, xa);
   }
-  uint32_t ready = 1;
   u32x4 bpre[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   const rsrc_t br = make_rsrc(B, (int64_t)d_out * r * 2);
   auto load_b = [&](int k) {
-    const int row0 = (cid + k * G) * 16;
+    const int row = (cid + k * G) * 16 + li;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int j = 32 * q + 8 * g;
-      const bool ok = j < r && row0 + li < d_out && k < nrt;
-      bpre[q] = bld16(br, ok ? (uint32_t)(((row0 + li) * r + j) * 2) : kOOB);
+      const bool ok = j < r && row < d_out;
+      bpre[q] = bld16(br, ok ? (uint32_t)((row * r + j) * 2) : kOOB);
     }
   };
-  if (P > 0 && wave == 0) {
-    ready = ld_dev_u32(&sync[1]);
-    load_b(0);
-  }
+  if (P > 0 && wave == 0) load_b(0);
 
-  // ---------------- adapter producer job (first P workgroups) ----------------
-  if (cid < P) {
-    const int j = cid / ksp, ks = cid % ksp;
-    const int nrow = r - 16 * j < 16 ? r - 16 * j : 16;
-    const rsrc_t ar = make_rsrc(A + (int64_t)16 * j * d_in, (int64_t)nrow * d_in * 2);
-    const int nk32 = d_in / 32;
-    const int kb = nk32 * ks / ksp, ke = nk32 * (ks + 1) / ksp;
+  // ---------------- adapter producer job ----------------
+  // The partial of columns 16j..16j+15 of u = x A^T over K slice ks: the
+  // waves split the slice and reduce through LDS; each float32 value goes out
+  // with this launch's tag in one 64-bit store. Nothing waits for those
+  // stores: a reader accepts an entry once its tag matches.
+  const uint32_t tag = launch_tag();
+  // x comes straight from global memory (rows >= T read zeros), so the job
+  // waits for nothing but its own loads, issued first.
+  if (producer) {
     f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kb + wave; k0 < ke; k0 += 4 * kW) {
-      u32x4 a[4], b[4];
+    for (int b = 0;; ++b) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k32 = k0 + kW * s;
-        const uint32_t off = k32 < ke ? (uint32_t)((li * d_in + k32 * 32 + 8 * g) * 2) : kOOB;
-        a[s] = bld16(xr, off);
-        b[s] = bld16(ar, off);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) pacc = mfma16(a[s], b[s], pacc);
+      for (int s = 0; s < kABatch; ++s)
+        if (k32b + wave + kW * (kABatch * b + s) < k32e) pacc = mfma16(xp[s], ap[s], pacc);  // wave-uniform
+      if (k32b + kABatch * kW * (b + 1) >= k32e) break;
+      a_issue(b + 1);
     }
+    // lane (li, g) holds u[4g + i][16j + li]
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + li] = pacc[i];
-    __syncthreads();
+    lds_barrier();
     if (tid < 256) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kW; ++w) v += red[w][tid];
-      const int t = tid >> 4, col = 16 * j + (tid & 15);
-      st_dev(upart + (ks * 16 + t) * r_pad + col, v);
+      const int t = tid >> 4, col = 16 * pj + (tid & 15);
+      if (t < T) st_dev_u64(uex + (pks * 16 + t) * r_pad + col, (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32));
     }
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = add_dev_u32(&sync[0], 1u);
-      if (prev == (uint32_t)P - 1u) {
-        st_dev_u32(&sync[0], 0u);
-        st_dev_u32(&sync[1], 1u);
-      }
-    }
+    lds_barrier();
   }
 
-  // ---------------- stage x in LDS ----------------
-  if (kXL) {
-    for (int c0 = tid * 8; c0 < d_in; c0 += kThreads * 8) {
-      u32x4 v[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) v[t] = bld16(xr, t < T ? (uint32_t)((t * d_in + c0) * 2) : kOOB);
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (t < T) st16(x_l + t * xpitch + c0, v[t]);
+  if (kXL && mseg > 0) {
+    x_store(0);
+    for (int j0 = kXSeg; j0 < mseg; j0 += kXSeg) {
+      x_issue(j0);
+      x_store(j0);
     }
-    __syncthreads();
   }
+  // This wave reads back only what it wrote: order its LDS stores before its
+  // loads without involving the other waves.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+  // ---------------- s*u exchange: read ahead, check at the first row-tile end ----------------
+  // Thread tid owns entries (t, col) = tid + i kThreads of the T x r_pad
+  // intermediate and reads their kKsp partials; the first kPairsAhead go out
+  // before the last item of the first row tile.
+  const int npair = T * r_pad;
+  uint64_t pv[kPairsAhead][kKsp];
+  auto poll_load = [&](int i, uint64_t (&dst)[kKsp]) {
+    const int p = tid + i * kThreads;
+    const int t = p / r_pad, col = p - t * r_pad;
+#pragma unroll
+    for (int ks = 0; ks < kKsp; ++ks)
+      dst[ks] = p < npair ? ld_dev_u64(uex + (ks * 16 + t) * r_pad + col) : ((uint64_t)tag << 32);
+  };
+  bool polled = false;
+  auto poll_issue = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPairsAhead; ++i) poll_load(i, pv[i]);
+    polled = true;
+  };
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int s, const GemvCodes &cs, const GemvX &xs) {
-    const Nf4Planes t = make_planes(c, restore_scale(cs.q2, cs.S));
+  auto compute = [&](int s, const GemvCodes &cs, const GemvX &xs2) {
+    const Nf4Planes t = make_planes(restore_scale(cs.q2, cs.S));
     // LDS path: token rows >= T only feed accumulator rows that are never stored,
     // and a block past the row end has an all-zero restore table, so both read
-    // clamped in-range x without masking.
-    const int kbl = 4 * (wave + kW * s) + g;
-    const uint16_t *xp = x_l + (li < T ? li : 0) * xpitch + (kbl < KB ? kbl : KB - 1) * kBlock;
+    // clamped, staged x without masking
+    // (a block past the row end reads the segment's first block, which this wave staged)
+    const int kbl = 4 * (wv + kW * s) + g;
+    const uint16_t *xq = x_l + (li < T ? li : 0) * xpitch + (kbl < KB ? kbl : 4 * (wv + kW * s)) * kBlock;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const u32x4 a = kXL ? *reinterpret_cast<const u32x4 *>(xp + 8 * m) : xs.x[m];
+      const u32x4 a = kXL ? *reinterpret_cast<const u32x4 *>(xq + 8 * m) : xs2.x[m];
       acc = mfma16(a, expand8(t, m < 4 ? cs.c0[m] : cs.c1[m - 4]), acc);
     }
   };
@@ -202,42 +288,52 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     const int row0 = (cid + k * G) * 16;
     const int rows = d_out - row0 < 16 ? d_out - row0 : 16;
     if (P > 0 && k == 0) {
-      // s*u for all rows of this workgroup: wave 0 waits for the producers, then
-      // every thread sums a few entries over the K-slice partials in slice order
-      // (deterministic) and stages bf16 s*u in LDS.
-      if (wave == 0) {
-        int it = 0;
-        while (ready == 0u) {
-          if (++it > kSpinLimit) {
-            st_dev_u32(&sync[3], 1u);
-            break;
+      // bf16(s*u) rows t < T into LDS once every tag matches: u is the sum of
+      // the kKsp partials in slice order (the same on every workgroup);
+      // workgroup 0 also writes float32 u. Rows t >= T of su_l only feed
+      // accumulator rows that are never stored.
+      if (!polled) poll_issue();
+      for (int it = 0;; ++it) {
+        int bad = 0;
+        for (int i = 0; i * kThreads < npair; ++i) {
+          uint64_t e[kKsp];
+          if (i < kPairsAhead) {
+#pragma unroll
+            for (int ks = 0; ks < kKsp; ++ks) e[ks] = pv[i < kPairsAhead ? i : 0][ks];
+          } else {
+            poll_load(i, e);
           }
-          __builtin_amdgcn_s_sleep(1);
-          ready = ld_dev_u32(&sync[1]);
-        }
-      }
-      __syncthreads();
-      const rsrc_t ur = make_rsrc(upart, (int64_t)ksp * 16 * r_pad * 4);
-      for (int e = tid; e < 16 * r_pad; e += kThreads) {
-        const int t = e / r_pad, col = e - t * r_pad;
-        float pv[kMaxKsp];
+          const int p = tid + i * kThreads;
+          bool ok = true;
+          float u = 0.f;
 #pragma unroll
-        for (int q = 0; q < kMaxKsp; ++q)
-          pv[q] = __uint_as_float(bld32_dev(ur, q < ksp ? (uint32_t)(((q * 16 + t) * r_pad + col) * 4) : kOOB));
-        float v = 0.f;
-#pragma unroll
-        for (int q = 0; q < kMaxKsp; ++q) v += pv[q];
-        if (u_out && cid == 0 && t < T && col < r) u_out[t * r + col] = v;
-        su_l[e] = (uint16_t)(pack_bf16x2((t < T && col < r) ? scale * v : 0.f, 0.f) & 0xffffu);
-      }
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t prev = add_dev_u32(&sync[2], 1u);
-        if (prev == (uint32_t)G - 1u) {
-          st_dev_u32(&sync[2], 0u);
-          st_dev_u32(&sync[1], 0u);
+          for (int ks = 0; ks < kKsp; ++ks) {
+            ok = ok && (uint32_t)(e[ks] >> 32) == tag;
+            u += __uint_as_float((uint32_t)e[ks]);
+          }
+          if (!ok) {
+            bad = 1;
+          } else if (p < npair) {
+            const int t = p / r_pad, col = p - t * r_pad;
+            su_l[t * r_pad + col] = (uint16_t)(pack_bf16x2(col < r ? scale * u : 0.f, 0.f) & 0xffffu);
+            if (u_out && cid == 0 && col < r) u_out[t * r + col] = u;
+          }
         }
+        // workgroup OR of `bad` (two flag rows in turn: a row is rewritten only
+        // two barriers after it was last read)
+        const int wbad = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0ull ? 1 : 0);
+        if (lane == 0) poll_bad[it & 1][wave] = wbad;
+        lds_barrier();
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) any |= poll_bad[it & 1][w];
+        if (!any) break;
+        if (it >= kSpinLimit) {
+          if (tid == 0) st_dev_u32(&sync[3], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        poll_issue();
       }
     }
     if (P > 0 && wave == 0) {
@@ -260,7 +356,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + li] = acc[i];
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
+    lds_barrier();
     if (tid < 256) {
       float v = 0.f;
 #pragma unroll
@@ -268,7 +364,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       const int t = tid >> 4, rl = tid & 15;
       if (t < T && rl < rows) h[t * d_out + row0 + rl] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   if (mseg == 0) {
@@ -281,6 +377,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       if (s2 == mseg) { s2 = 0; ++k2; }
       load_codes(k2, s2, cb);
       if (!kXL) load_x(s2, xb);
+      if (P > 0 && k == 0 && s == mseg - 1) poll_issue();
       compute(s, ca, xa);
       if (s == mseg - 1) epilogue(k);
       k = k2, s = s2;
@@ -290,34 +387,16 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       if (s2 == mseg) { s2 = 0; ++k2; }
       load_codes(k2, s2, ca);
       if (!kXL) load_x(s2, xa);
+      if (P > 0 && k == 0 && s == mseg - 1) poll_issue();
       compute(s, cb, xb);
       if (s == mseg - 1) epilogue(k);
       k = k2, s = s2;
       if (k >= nrt) break;
     }
   }
-  if (P > 0 && nrt == 0 && tid == 0) {
-    // a workgroup without rows still takes part in the handshake count
-    const uint32_t prev = add_dev_u32(&sync[2], 1u);
-    if (prev == (uint32_t)G - 1u) {
-      st_dev_u32(&sync[2], 0u);
-      st_dev_u32(&sync[1], 0u);
-    }
-  }
 }
 
-#ifndef QLORA_GEMV_WAVES
-#define QLORA_GEMV_WAVES 8
-#endif
-constexpr int kGvW = QLORA_GEMV_WAVES;  // waves per workgroup
-
-int gemv_ksplit(int64_t d_in) {
-  // one batch of <= 4 K steps per producer wave where possible
-  int64_t ksp = (d_in / 32 + 4 * kGvW - 1) / (4 * kGvW);
-  if (ksp < 1) ksp = 1;
-  if (ksp > kMaxKsp) ksp = kMaxKsp;
-  return (int)ksp;
-}
+constexpr int kGvW = 8;  // waves per workgroup
 
 static int g_gemv_cus[64];
 static bool g_gemv_attr[64];
@@ -337,14 +416,18 @@ static int device_cus(int dev) {
   return cus;
 }
 
+bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T) {
+  // whole-tensor buffer ranges: packed codes (and the rows of one ragged tile) below 2^31 bytes
+  return T >= 1 && T <= 16 && (d_out + 16) * d_in / 2 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B, int r,
-                           int r_pad, float scale, uint16_t *h, float *u_out, float *upart, uint32_t *sync,
-                           const Nf4Consts &c, hipStream_t st) {
-  if (r_pad > kMaxRpad) return hipErrorInvalidValue;
+                           int r_pad, float scale, uint16_t *h, float *u_out, uint64_t *uex, uint32_t *sync,
+                           hipStream_t st) {
+  if (r_pad > kMaxRpad || !gemv_supported(d_out, d_in, T)) return hipErrorInvalidValue;
   const int dev = device_index();
-  const int ksp = gemv_ksplit(d_in);
-  const int P = r > 0 ? (r_pad / 16) * ksp : 0;
+  const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
   const int64_t RT = (d_out + 15) / 16;
   // One workgroup per CU; the first P of them also produce x A^T. The grid never
   // exceeds one residency, so every workgroup runs concurrently.
@@ -360,10 +443,10 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
       g_gemv_attr[dev] = true;
     }
     k_gemv_fwd<kGvW, true><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
-        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, ksp, scale, h, u_out, upart, sync, c);
+        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
   } else {
     k_gemv_fwd<kGvW, false><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
-        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, ksp, scale, h, u_out, upart, sync, c);
+        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
   }
   return hipGetLastError();
 }

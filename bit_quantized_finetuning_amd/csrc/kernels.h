@@ -28,19 +28,19 @@ hipError_t launch_lora_small(const uint16_t *P, const uint16_t *Q, int64_t T, in
 hipError_t launch_transpose_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst,
                                  hipStream_t st);
 
-// gemv.hip: T <= 16, one launch (or one per residency-sized chunk of rows):
+// gemv.hip: T <= 16, one launch:
 // h[T, d_out] = x W_hat^T + scale (x A^T) B^T. u_out (nullable) receives x A^T
-// [T, r]; upart is a [gemv_ksplit(d_in), 16, r_pad] float32 exchange buffer
-// for the adapter intermediate; sync points at the four
-// handshake words (zero before the call, left zero after it; word 3 records a
-// timed-out wait).
+// [T, r]. uex is the [4, 16, r_pad] exchange buffer of tagged float32 partials
+// of x A^T (one per quarter of K); sync points at four reserved words (word 3
+// is set if a bounded wait timed out).
 hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B, int r,
-                           int r_pad, float scale, uint16_t *h, float *u_out, float *upart, uint32_t *sync,
-                           const Nf4Consts &c, hipStream_t st);
-int gemv_ksplit(int64_t d_in);
+                           int r_pad, float scale, uint16_t *h, float *u_out, uint64_t *uex, uint32_t *sync,
+                           hipStream_t st);
+// Whether the T <= 16 kernel takes these sizes (its buffer ranges cover whole tensors).
+bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T);
 
-// gemm.hip: T > 16.
+// gemm.hip: T > 16 (and any T the weight-streaming kernel does not take).
 hipError_t launch_gemm_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *su, int r_pad,
                            const uint16_t *B, int r, uint16_t *h, const Nf4Consts &c, hipStream_t st);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
     const int64_t blk = i >> 3;
     const float sh = restore_scale(qscale[blk], smax[blk >> 8]);
     if (kBf16Out) {
-      const Nf4Planes t = make_planes(c, sh);
+      const Nf4Planes t = make_planes(sh);
       st16(static_cast<uint16_t *>(out) + i * 8, expand8(t, cw));
     } else {
       f32x4 a, b;

@@ -23,8 +23,8 @@ BLOCK = 64
 GROUP = 256
 MAX_RANK = 256
 # The workspace starts with a counter region (u32 words) that must be zero before
-# the first call and that every call leaves zero; its last four words are the
-# skinny-token forward's producer/consumer handshake (word 3 = a timed-out wait).
+# the first call and that every call leaves zero; its last word is set only if a
+# bounded wait of the skinny-token forward timed out.
 COUNTER_BYTES = 16384 * 4
 
 F32, BF16 = 0, 1

@@ -53,7 +53,9 @@ typedef enum {
   QLORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned               */
   QLORA_ERR_WORKSPACE = -4, /* ws_bytes < qlora_workspace_bytes(...)          */
   QLORA_ERR_DTYPE = -5,     /* unknown dtype enum                             */
-  QLORA_ERR_HIP = -6        /* a kernel launch failed                         */
+  QLORA_ERR_HIP = -6,       /* a kernel launch failed                         */
+  QLORA_ERR_INTERNAL = -7   /* the levels compiled into the kernels differ from
+                               the table derived at load (never expected)      */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -109,9 +111,9 @@ int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStr
  *   ws     device workspace of at least qlora_workspace_bytes(d_out, d_in, T, r)
  *          bytes. Its first QLORA_WS_COUNTER_BYTES bytes are u32 counters that
  *          must be zero before the first use of the workspace; every call leaves
- *          them zero again. The last four of those words are the handshake of
- *          the T <= 16 kernel; word 3 becomes nonzero only if a bounded wait in
- *          that kernel timed out (the call's output is then unspecified).
+ *          them zero again. The last of them becomes nonzero only if a bounded
+ *          wait in the T <= 16 kernel timed out (the call's output is then
+ *          unspecified). The rest of the workspace needs no initialisation.
  * T <= 16 runs one weight-streaming kernel (the adapter intermediate is formed
  * by the first workgroups of the same launch); larger T runs the MFMA GEMM.
  */

@@ -139,10 +139,10 @@ def test_forward_parity(d_out, d_in, r, T):
 
 
 def _assert_workspace_clean():
-    """Every counter and the skinny forward's handshake words are back to zero after a call."""
+    """After a call every counter is back to zero and no bounded wait timed out."""
     ws = q.workspace("cuda", 1 << 20)
     counters = ws[:q.COUNTER_BYTES].view(torch.int32)
-    assert int(counters.abs().sum().item()) == 0, "counter / handshake region not reset"
+    assert int(counters.abs().sum().item()) == 0, "counter region not reset (or a wait timed out)"
 
 
 @pytest.mark.parametrize("d_out,d_in,r", SHAPES)
@@ -231,3 +231,20 @@ def test_error_leaves_outputs_untouched():
     torch.cuda.synchronize()
     assert st == -4
     assert bool((h == 7.0).all())
+
+
+def test_skinny_forward_call_sequence():
+    """Back-to-back T <= 16 calls with changing adapters, ranks and shapes on one workspace: each
+    result matches the oracle, so no call accepts the adapter intermediate of an earlier one."""
+    seq = [(272, 320, 64, 16, 111), (272, 320, 64, 16, 112), (80, 192, 16, 4, 113), (272, 320, 64, 1, 114),
+           (528, 1344, 256, 16, 115), (272, 320, 8, 16, 116)]
+    for d_out, d_in, r, T, cfg in seq:
+        say(f"sequence {d_out}x{d_in} r={r} T={T} cfg={cfg}")
+        case = Case(d_out, d_in, r, T, cfg=cfg)
+        w, d = _quantize_and_compare(case)
+        h, u = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha, save_u=True)
+        torch.cuda.synchronize()
+        h_ref, u_ref = case.oracle_forward()
+        assert_close("h", h, h_ref)
+        assert_close("u", u, u_ref)
+    _assert_workspace_clean()
