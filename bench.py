@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--chunk", type=int, default=20, help="steps per captured graph")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-per-call", action="store_true", help="skip the per-call-shape timings (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
@@ -212,7 +213,8 @@ def main():
         us_launch = ms_total * 1e3 / launches
         achieved = (fb / len(calls)) / (us_launch * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic() if args.workload == "llama7b_skinny" else None,
                 "kernel": "k_gemv_fwd (qlora_forward, T <= 16)",
                 "bytes_per_launch": round(fb / len(calls)), "us_per_launch": round(us_launch, 3),
                 "launches": launches}
@@ -222,10 +224,12 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "kernel": "whole forward + backward step (all kernels)"}
 
-    per_call = per_call_times(torch, dev, calls, run_call, chunk) if not args.no_graph else []
+    per_call = per_call_times(torch, dev, calls, run_call, chunk) if not (args.no_graph or args.no_per_call) else []
 
     if args.copy_calibration:
-        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        # a plain device copy of known size (256 MiB read + 256 MiB written per launch), the reference that
+        # scales the HBM byte counters
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
@@ -260,6 +264,26 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_k_gemv_fwd_llama7b_skinny.json")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the weight-streaming kernel from the recorded FETCH_SIZE / WRITE_SIZE runs,
+    or None when the record is missing or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def per_call_times(torch, dev, calls, run_call, chunk):
