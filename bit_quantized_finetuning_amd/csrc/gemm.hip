@@ -340,10 +340,6 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint8_t *__restrict__ cod
 
   const int64_t mrows = T - m0 < kBM ? T - m0 : kBM;
   const rsrc_t yr = make_rsrc(dY + m0 * d_out, mrows * d_out * 2);
-  // whole weight (the caller keeps the packed codes below 2^31 bytes)
-  const rsrc_t cr = make_rsrc(codes, d_out * (d_in / 2));
-  const rsrc_t qr = make_rsrc(qscale, d_out * KB);
-  const rsrc_t sr = make_rsrc(smax, ((d_out * KB + kGroup - 1) / kGroup) * 4);
 
   const int xr_ = tid >> 3, xc = (tid & 7) * 8;
   const int wo = tid >> 2, wb = tid & 3;  // weight tile: row o, block b (64 columns)
@@ -356,13 +352,19 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint8_t *__restrict__ cod
       const bool ok = kt < nk && k0 + xc < d_out;
       R.y[i] = bld16(yr, ok ? (uint32_t)(((xr_ + 32 * i) * d_out + k0 + xc) * 2) : kOOB);
     }
-    const int64_t o = k0 + wo;
-    const bool ok = kt < nk && o < d_out && kblk < KB;
-    const uint32_t blk = (uint32_t)(o * KB + kblk);
-    R.c0 = bld16(cr, ok ? blk * 32u : kOOB);
-    R.c1 = bld16(cr, ok ? blk * 32u + 16u : kOOB);
-    R.q2 = bld8(qr, ok ? blk : kOOB);
-    R.S = __uint_as_float(bld32(sr, ok ? (blk >> 8) * 4u : kOOB));
+    // weight rows k0..k0+63: ranges rebased per K tile (32-bit offsets stay small for any weight size)
+    const int64_t orows = kt < nk ? (d_out - k0 < kBK ? d_out - k0 : kBK) : 0;
+    const int64_t kr = kt < nk ? k0 : 0;
+    const rsrc_t cr = make_rsrc(codes + kr * (d_in / 2), orows * (d_in / 2));
+    const rsrc_t qr = make_rsrc(qscale + kr * KB, orows * KB);
+    const int64_t gb = (kr * KB) >> 8;  // first group of the tile's rows
+    const rsrc_t sr = make_rsrc(smax + gb, ((d_out * KB + kGroup - 1) / kGroup - gb) * 4);
+    const bool ok = wo < orows && kblk < KB;
+    const uint32_t lblk = (uint32_t)(wo * KB + kblk);  // block index within the tile
+    R.c0 = bld16(cr, ok ? lblk * 32u : kOOB);
+    R.c1 = bld16(cr, ok ? lblk * 32u + 16u : kOOB);
+    R.q2 = bld8(qr, ok ? lblk : kOOB);
+    R.S = __uint_as_float(bld32(sr, ok ? (uint32_t)((((kr * KB) & (kGroup - 1)) + lblk) >> 8) * 4u : kOOB));
   };
   auto restore = [&](const DxRegs &R, int buf) {
     uint16_t *as = As + buf * kBM * kAP;
