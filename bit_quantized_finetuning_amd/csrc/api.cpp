@@ -137,6 +137,9 @@ Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
     pf = std::max(pf, lora_grad_partial_floats(r, d_in, T));
     pf = std::max(pf, lora_grad_partial_floats(d_out, r, T));
   }
+  // K-split tail tiles of the large-T contractions (forward over d_in, dX over d_out)
+  pf = std::max(pf, gemm_partial_floats(gemm_plan(T, d_out, d_in / kBlock)));
+  pf = std::max(pf, gemm_partial_floats(gemm_plan(T, d_in, ceil_div(d_out, kBlock))));
   L.partial = off;
   off = align256(off + pf * 4);
   L.total = off;
@@ -226,7 +229,6 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   if (!ws) return QLORA_ERR_NULL;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
 
-  const Nf4Consts &c = consts();
   const int rp = rank_pad(r);
   const float sc = r > 0 ? alpha / (float)r : 0.f;
   if (gemv_supported(d_out, d_in, T))
@@ -241,7 +243,8 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
     e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
-  e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, c, stream);
+  e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
+                      at<uint32_t>(ws, 0), stream);
   return hip_status(e);
 }
 
@@ -269,7 +272,6 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (!dX && !dA && !dB) return QLORA_OK;
 
-  const Nf4Consts &c = consts();
   const int rp = rank_pad(r);
   const float sc = r > 0 ? alpha / (float)r : 0.f;
   uint16_t *sv = at<uint16_t>(ws, L.sx);
@@ -287,7 +289,8 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dX) {
-    e = launch_gemm_dx(W->codes, W->qscale, W->smax, d_out, d_in, dY, T, sv, rp, A, r, dX, c, stream);
+    e = launch_gemm_dx(W->codes, W->qscale, W->smax, d_out, d_in, dY, T, sv, rp, A, r, dX, partial,
+                       at<uint32_t>(ws, 0), stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dA) {

@@ -178,6 +178,14 @@ __device__ __forceinline__ uint32_t bld32_dev(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t bld8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
+// Loads at a per-lane offset plus a wave-uniform one (an SGPR operand), for
+// addresses known to lie inside the range.
+__device__ __forceinline__ u32x4 bld16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bld8s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup exchange inside one launch, without cache-wide fences: the

@@ -11,63 +11,285 @@
 // discarded). The adapter term enters as extra K columns: [x | su] . [W_hat | B]^T
 // and [dY | sv] . [W_hat ; A].
 //
-// Tiling: a 512-thread workgroup computes a 256 x 256 output tile; its eight
-// waves (two per SIMD) each own 128 x 64 (4 x 2 v_mfma_f32_32x32x16_bf16
-// tiles). With two waves on a SIMD, one wave's restore VALU issues while the
-// other's MFMAs occupy the matrix core. K advances 64 at a time:
-//   * global loads run two tiles ahead (two register sets in turn), so a tile's
-//     codes and activations have a whole K step to arrive;
-//   * LDS is double-buffered: while the MFMAs consume tile k, the waves restore
-//     tile k+1 into the other buffer, two lanes per 64-weight block (32 weights
-//     each). The restore is cut into pieces of a few VALU instructions, one
-//     after each MFMA, with scheduling fences that keep the order;
-//   * loop bodies are straight-line: tiles past the end load zeros (out-of-range
-//     buffer offsets) and add nothing.
-// Forward: W's K (= d_in) runs along a block, so a restored block is one row of
-// the K-contiguous weight tile and the MFMA B operand is read straight from LDS.
-// dX: K = d_out runs across blocks; the restored tile is stored [o][i] as
-// restored and the B fragments (8 consecutive o for one i per lane) come from
-// two ds_read_b64_tr_b16, which transpose 16-bit data across each 16 lanes.
+// Tiling: a 256-thread workgroup (four waves, one per SIMD) computes a 256 x 256
+// output tile; wave w owns all 256 rows and columns 64w .. 64w+63 (8 x 2
+// v_mfma_f32_32x32x16_bf16 tiles, 256 accumulators per lane). K advances 64 at
+// a time. On gfx950 the matrix cores are starved first by LDS stores (they
+// stall MFMA issue), then by LDS reads; VALU work co-issues with MFMAs almost
+// for free. Hence:
+//   * activation tiles (x, dY, su, sv) go from memory straight into LDS with
+//     buffer_load ... lds (no registers, no LDS store instructions), two tiles
+//     in a ring: the copy of step k+1 runs during step k;
+//   * forward: a wave's B operand (8 consecutive K of one output row per lane)
+//     is exactly one 32-bit word of packed codes, so each lane restores its own
+//     fragments in registers from its codes and block scale; no weight tile
+//     touches LDS and every weight is restored once per workgroup;
+//   * dX: K = d_out runs across weight rows, so a lane's fragment needs one
+//     nibble from each of 8 rows. The workgroup restores the 64 x 256 weight
+//     tile of step k+1 into LDS during step k (one 64-weight block per lane)
+//     and the waves read B fragments with ds_read_b64_tr_b16, which transposes
+//     16-bit data across each 16 lanes;
+//   * the K order inside a step is permuted the same way for both operands:
+//     slice s, lane half h covers K columns 32h + 8s .. +7, so a lane's four
+//     forward code words of a step are one 16-byte load;
+//   * the restore and the fragment reads of the next slice are cut into pieces
+//     of a few instructions, one after each MFMA, with scheduling fences that
+//     keep the order; the one barrier per step sits in the middle of the last
+//     slice so that the matrix core keeps working across it.
 // The epilogue goes through LDS so that every lane writes 16-byte rows.
 #include "kernels.h"
 
 namespace qlora {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kWM = 128, kWN = 64;  // wave tile
-constexpr int kAP = kBK + 8;   // padded pitch (bf16) of [row][k] tiles: fragment reads free of bank conflicts
-constexpr int kBTP = kBN + 16; // pitch of the dX [k][n] weight tile: the four rows of a transposed read 8 banks apart
-constexpr int kEP = kWN + 8;   // epilogue staging pitch (bf16) of a wave's 128 x 64 tile
-constexpr size_t kStageLds = (size_t)kWaves * kWM * kEP * sizeof(uint16_t);
+constexpr int kThreads = 256;                 // four waves, one per SIMD
+constexpr int kWN = 64;                       // output columns per wave
+constexpr int kTile = kBM * kBK * 2;          // bytes of one swizzled 256 x 64 bf16 activation tile
+constexpr int kWRow = kBN * 2;                // bytes per row of the dX [k][n] weight tile (unpadded)
+constexpr int kWTile = kBK * kWRow;           // bytes of one dX weight tile
+constexpr int kEP = kWN + 8;                  // epilogue staging pitch (bf16)
+constexpr size_t kStageLds = (size_t)4 * kBM * kEP * 2;
+constexpr size_t kFwdTiles = (size_t)2 * kTile;
+constexpr size_t kDxTiles = (size_t)2 * kTile + (size_t)2 * kWTile;
+constexpr size_t kFwdLds = kFwdTiles > kStageLds ? kFwdTiles : kStageLds;
+constexpr size_t kDxLds = kDxTiles > kStageLds ? kDxTiles : kStageLds;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// One wave's 128 x 64 fp32 tile -> bf16 rows of `out` (row pitch ld, rows < mlim,
-// columns < nlim), staged through this wave's LDS region so that each lane
-// stores 16 contiguous bytes. Lane l, accumulator e of tile (i, j) holds row
-// 32i + 8(e/4) + 4(l/32) + e%4, column 32j + l%32.
-__device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[4][2], uint16_t *stage, int lane,
-                                                uint16_t *out, int64_t ld, int64_t row0, int64_t col0,
-                                                int64_t mlim, int64_t nlim) {
+#define QLORA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Pin a value to this point of the instruction stream: an empty volatile asm
+// that reads and rewrites it. Scheduling fences order only instructions with
+// side effects; pure arithmetic would otherwise drift to its first use (or up
+// to its inputs). Pinning a piece's inputs before it and its results after it
+// keeps each restore piece between the MFMAs it was written between.
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x4 &x) { asm volatile("" : "+v"(x)); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all of its LDS operations are done, then join the workgroup barrier. One
+// asm block with a memory clobber: no LDS access moves across it, and the
+// copies into LDS still in flight (the newest N operations) are not waited for.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Activation tiles in LDS: row r (0..255) takes 128 bytes at 128 r; its 16-byte
+// chunk c (K columns 8c .. 8c+7) sits at chunk position c ^ swz(r), which puts
+// the 16 rows of one fragment read on 16 distinct bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Copies of rows 0..255, K columns k0 .. k0+63 of a bf16 matrix (row pitch
+// `pitch` elements; the buffer range covers the valid rows, rows past it read
+// zeros) into a swizzled tile. Wave w issues 8 copies of 1 KB (8 rows each);
+// lane L fills row 8g + L/8, chunk position L%8. DmaOffs holds each lane's
+// source byte offsets for k0 = 0; full tiles add 2 k0 as the scalar offset.
+struct DmaOffs {
+  uint32_t v[8];
+};
+__device__ __forceinline__ DmaOffs dma_offsets(int pitch, int wave, int lane) {
+  DmaOffs o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * (8 * wave + q) + (lane >> 3);
+    o.v[q] = (uint32_t)(r * pitch + 8 * ((lane & 7) ^ swz(r))) * 2u;
+  }
+  return o;
+}
+// Tile with K columns k0 .. k0+63 all below klim: no per-lane checks.
+__device__ __forceinline__ void dma_tile(rsrc_t src, const DmaOffs &o, int k0, uint8_t *tile, int wave) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)(tile + 1024 * (8 * wave + q)), 16, o.v[q],
+                                             2 * k0, 0, 0);
+}
+// Tile reaching past klim (a K tail): chunks at or past klim read zeros.
+__device__ __forceinline__ void dma_tile_tail(rsrc_t src, const DmaOffs &o, int k0, int klim, uint8_t *tile,
+                                              int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * (8 * wave + q) + (lane >> 3);
+    const int c8 = 8 * ((lane & 7) ^ swz(r));
+    const uint32_t keep = (uint32_t)((c8 - (klim - k0)) >> 31);  // all ones if k0 + c8 < klim
+    const uint32_t off = ((o.v[q] + 2u * (uint32_t)k0) & keep) | (kOOB & ~keep);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)(tile + 1024 * (8 * wave + q)), 16, off, 0, 0, 0);
+  }
+}
+// The same copies issued from inline asm, for kernels that also read LDS with
+// ds_read_b64_tr_b16: the compiler makes every such read wait for all copies
+// into LDS it knows of, which would stall the first transposed read of a step
+// until the next step's tile has landed. Copies it does not see impose no such
+// wait; the kernel orders them itself (barrier waits with explicit counts) and
+// waits for vmcnt(0) before issuing them, so that the counts the compiler
+// keeps for its own loads never span a copy.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const int n = bytes >= 0x7fffffffll ? 0x7fffffff : (int)bytes;
+  // same descriptor as make_rsrc: 48-bit base, stride 0, range n, raw 32-bit format
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), n, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+__device__ __forceinline__ void dma16_asm(const i32x4 &rs, uint32_t m0v, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");  // M0 is reserved (never allocated); nothing else in the kernels that use this reads it
+}
+// Checked copies (chunks at or past klim read zeros) from asm.
+__device__ __forceinline__ void dma_tile_asm(const i32x4 &rs, const DmaOffs &o, int k0, int klim, uint8_t *tile,
+                                             int wave, int lane) {
+  const uint32_t base = lds_addr(tile);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * (8 * wave + q) + (lane >> 3);
+    const int c8 = 8 * ((lane & 7) ^ swz(r));
+    const uint32_t keep = (uint32_t)((c8 - (klim - k0)) >> 31);  // all ones if k0 + c8 < klim
+    const uint32_t off = ((o.v[q] + 2u * (uint32_t)k0) & keep) | (kOOB & ~keep);
+    dma16_asm(rs, base + 1024u * (uint32_t)(8 * wave + q), off, 0u);
+  }
+}
+
+__device__ __forceinline__ void dma_any(rsrc_t src, const DmaOffs &o, int k0, int klim, uint8_t *tile, int wave,
+                                        int lane) {
+  if (k0 + kBK <= klim)
+    dma_tile(src, o, k0, tile, wave);
+  else
+    dma_tile_tail(src, o, k0, klim, tile, wave, lane);
+}
+
+// Byte offset (within a tile) of lane (m = l%32, h = l/32)'s A fragment of
+// slice s in row tile 0; row tile i adds 4096 i. The fragment holds row m,
+// K columns 32h + 8s .. +7 (chunk 4h + s).
+__device__ __forceinline__ int a_off(int lane, int s) {
+  const int m = lane & 31, h = lane >> 5;
+  return m * 128 + (((4 * h + s) ^ swz(m)) << 4);
+}
+
+// Restore-table build of one 64-weight block cut into 3 pieces: products of
+// the first and second half of the 16 levels, then the byte planes.
+struct TableBuild {
+  float sh;
+  uint32_t p[8];
+  __device__ __forceinline__ void run(int k, uint32_t q2, float S, Nf4Planes &t) {
+    if (k == 0) {
+      pin(q2);
+      pin(S);
+      sh = restore_scale(q2, S);
+      pin(sh);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = pack_bf16x2(code_times(2 * u, sh), code_times(2 * u + 1, sh));
+        pin(p[u]);
+      }
+    } else if (k == 1) {
+#pragma unroll
+      for (int u = 4; u < 8; ++u) {
+        p[u] = pack_bf16x2(code_times(2 * u, sh), code_times(2 * u + 1, sh));
+        pin(p[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        t.lo[u] = perm(p[2 * u + 1], p[2 * u], 0x06040200u);
+        t.hi[u] = perm(p[2 * u + 1], p[2 * u], 0x07050301u);
+        pin(t.lo[u]);
+        pin(t.hi[u]);
+      }
+    }
+  }
+};
+
+// expand8 cut into 4 pieces: selectors, low-plane lookups, high-plane
+// lookups, interleave (the result is complete after piece 3).
+struct Expand {
+  uint32_t sa, ma, sb, mb, lo_a, hi_a, lo_b, hi_b;
+  __device__ __forceinline__ void run(int ph, const Nf4Planes &t, uint32_t w, u32x4 &out) {
+    if (ph == 0) {
+      pin(w);
+      sa = w & 0x07070707u;
+      ma = ((w >> 1) & 0x04040404u) | 0x03020100u;
+      sb = (w >> 4) & 0x07070707u;
+      mb = ((w >> 5) & 0x04040404u) | 0x03020100u;
+      pin(sa);
+      pin(ma);
+      pin(sb);
+      pin(mb);
+    } else if (ph == 1) {
+      lo_a = lookup4(t.lo, sa, ma);
+      hi_a = lookup4(t.hi, sa, ma);
+      pin(lo_a);
+      pin(hi_a);
+    } else if (ph == 2) {
+      lo_b = lookup4(t.lo, sb, mb);
+      hi_b = lookup4(t.hi, sb, mb);
+      pin(lo_b);
+      pin(hi_b);
+    } else {
+      out[0] = perm(hi_a, lo_a, 0x05010400u);
+      out[1] = perm(hi_a, lo_a, 0x07030602u);
+      out[2] = perm(hi_b, lo_b, 0x05010400u);
+      out[3] = perm(hi_b, lo_b, 0x07030602u);
+      pin(out);
+    }
+  }
+};
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[8][2]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rr = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), cc = 32 * j + (lane & 31);
-        stage[rr * kEP + cc] = (uint16_t)(pack_bf16x2(acc[i][j][e], 0.f) & 0xffffu);
-      }
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+}
+
+// Epilogue through LDS: a wave's 256 x 64 tile is staged as bf16 rows in this
+// wave's region (pitch kEP), then written out so that each lane stores 16
+// contiguous bytes. Lane l, accumulator e of MFMA tile (i, j) holds row
+// 32i + 8(e/4) + 4(l/32) + e%4, column 32j + l%32.
+__device__ __forceinline__ void stage_put4(uint16_t *stage, int lane, int i, int j, int e4, float a0, float a1,
+                                           float a2, float a3) {
+  const int rr = 32 * i + 8 * e4 + 4 * (lane >> 5), cc = 32 * j + (lane & 31);
+  stage[rr * kEP + cc] = (uint16_t)(pack_bf16x2(a0, 0.f) & 0xffffu);
+  stage[(rr + 1) * kEP + cc] = (uint16_t)(pack_bf16x2(a1, 0.f) & 0xffffu);
+  stage[(rr + 2) * kEP + cc] = (uint16_t)(pack_bf16x2(a2, 0.f) & 0xffffu);
+  stage[(rr + 3) * kEP + cc] = (uint16_t)(pack_bf16x2(a3, 0.f) & 0xffffu);
+}
+__device__ __forceinline__ void stage_acc(const f32x16 (&acc)[8][2], uint16_t *stage, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        stage_put4(stage, lane, i, j, e4, acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                   acc[i][j][4 * e4 + 3]);
+}
+// Rows [rlo, rhi) of the staged tile -> `out` (row pitch ld; rows < mlim and
+// columns < nlim of the output).
+__device__ __forceinline__ void stage_store(const uint16_t *stage, int lane, uint16_t *out, int64_t ld,
+                                            int64_t row0, int64_t col0, int64_t mlim, int64_t nlim, int rlo,
+                                            int rhi) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  // 128 rows x 8 chunks of 8 bf16: lane takes chunk lane%8 of rows lane/8 + 8q
+  // 256 rows x 8 chunks of 8 bf16: lane takes chunk lane%8 of rows lane/8 + 8q
 #pragma unroll 4
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < 32; ++q) {
     const int rr = (lane >> 3) + 8 * q, ch = lane & 7;
     const int64_t m = row0 + rr, n = col0 + 8 * ch;
-    if (m < mlim && n < nlim) {
+    if (rr >= rlo && rr < rhi && m < mlim && n < nlim) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + rr * kEP + 8 * ch);
       if (n + 8 <= nlim) {
         st16(out + m * ld + n, v);
@@ -79,135 +301,141 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[4][2], uint1
   }
 }
 
-// Half of a 64-weight block's restore (4 packed words, 32 weights) and four
-// activation chunks' LDS stores, cut into 25 pieces of a few VALU instructions
-// so that one piece can follow each MFMA of a K step. pieces 0..3: scale and
-// table products; 4: byte planes; 5 + 4m + 0..3: word m's selectors,
-// low-nibble lookups, high-nibble lookups, interleave and LDS store;
-// 21..24: the activation chunks.
-constexpr int kPieces = 25;
-struct PieceRestore {
-  float sh;
-  uint32_t p[8];
-  Nf4Planes t;
-  uint32_t sa, ma, sb, mb, lo_a, hi_a, lo_b, hi_b;
-  __device__ __forceinline__ void run(int k, uint32_t q2, float S, const u32x4 &c, uint16_t *wdst,
-                                      const u32x4 (&act)[4], uint16_t *const (&adst)[4]) {
-    if (k < 4) {
-      if (k == 0) sh = restore_scale(q2, S);
-      p[2 * k] = pack_bf16x2(code_times(4 * k, sh), code_times(4 * k + 1, sh));
-      p[2 * k + 1] = pack_bf16x2(code_times(4 * k + 2, sh), code_times(4 * k + 3, sh));
-    } else if (k == 4) {
+// The 64 MFMAs of an adapter K tile (operands from LDS / registers, no overlap).
+template <typename BFn>
+__device__ __forceinline__ void plain_tile(f32x16 (&acc)[8][2], const uint8_t *atile, const int (&aoff)[4],
+                                           BFn bfrag) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        t.lo[j] = perm(p[2 * j + 1], p[2 * j], 0x06040200u);
-        t.hi[j] = perm(p[2 * j + 1], p[2 * j], 0x07050301u);
-      }
-    } else if (k < 21) {
-      const int m = (k - 5) >> 2, ph = (k - 5) & 3;
-      const uint32_t w = c[m];
-      if (ph == 0) {
-        sa = w & 0x07070707u;
-        ma = ((w >> 1) & 0x04040404u) | 0x03020100u;
-        sb = (w >> 4) & 0x07070707u;
-        mb = ((w >> 5) & 0x04040404u) | 0x03020100u;
-      } else if (ph == 1) {
-        lo_a = lookup4(t.lo, sa, ma);
-        hi_a = lookup4(t.hi, sa, ma);
-      } else if (ph == 2) {
-        lo_b = lookup4(t.lo, sb, mb);
-        hi_b = lookup4(t.hi, sb, mb);
-      } else {
-        u32x4 r;
-        r[0] = perm(hi_a, lo_a, 0x05010400u);
-        r[1] = perm(hi_a, lo_a, 0x07030602u);
-        r[2] = perm(hi_b, lo_b, 0x05010400u);
-        r[3] = perm(hi_b, lo_b, 0x07030602u);
-        st16(wdst + 8 * m, r);
-      }
-    } else if (k < kPieces) {
-      st16(adst[k - 21], act[k - 21]);
-    }
-  }
-};
-#define QLORA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Register set of one K tile held by one lane: four 8-element activation
-// chunks and half a block of codes with its scale code and group maximum.
-struct TileRegs {
-  u32x4 a[4];
-  u32x4 c;
-  uint32_t q2;
-  float S;
-};
-
-// One K step of one wave: the 32 MFMAs of its 128 x 64 tile over LDS buffer
-// `buf`, each followed by one restore piece of register set R. Fragments of
-// the next 16-wide K slice are read while the current slice's MFMAs run: the
-// B pair one slice ahead, each A fragment as soon as its two MFMAs are issued.
-template <typename FragFn>
-__device__ __forceinline__ void k_step(f32x16 (&acc)[4][2], const FragFn &frags, int buf, const TileRegs &R,
-                                       uint16_t *wdst, uint16_t *const (&adst)[4]) {
-  PieceRestore pr;
-  u32x4 fa[4], fb[2][2];
-  frags.a_all(buf, 0, fa);
-  frags.b(buf, 0, fb[0]);
+  for (int s = 0; s < 4; ++s) {
+    u32x4 a[8], b[2];
 #pragma unroll
-  for (int k16 = 0; k16 < kBK / 16; ++k16) {
-    const bool more = k16 + 1 < kBK / 16;
-    if (more) frags.b(buf, k16 + 1, fb[(k16 + 1) & 1]);
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const u32x4 *>(atile + aoff[s] + 4096 * i);
+    bfrag(s, b);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = q >> 1, j = q & 1;
-      acc[i][j] = mfma32(fa[i], fb[k16 & 1][j], acc[i][j]);
-      QLORA_SCHED_FENCE();
-      pr.run(8 * k16 + q, R.q2, R.S, R.c, wdst, R.a, adst);
-      if (j == 1 && more) fa[i] = frags.a(buf, k16 + 1, i);
-      QLORA_SCHED_FENCE();
-    }
-  }
-}
-
-// The whole restore of register set R at once (before the first K step).
-__device__ __forceinline__ void restore_all(const TileRegs &R, uint16_t *wdst, uint16_t *const (&adst)[4]) {
-  PieceRestore pr;
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) pr.run(k, R.q2, R.S, R.c, wdst, R.a, adst);
-}
-
-// Adapter K slices: MFMAs over LDS buffer 0 without restore work.
-template <typename FragFn>
-__device__ __forceinline__ void k_plain(f32x16 (&acc)[4][2], const FragFn &frags) {
-#pragma unroll
-  for (int k16 = 0; k16 < kBK / 16; ++k16) {
-    u32x4 a[4], b[2];
-    frags.a_all(0, k16, a);
-    frags.b(0, k16, b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][2]) {
+// ---------------------------------------------------------------------------
+// Work items and K-split tails
+// ---------------------------------------------------------------------------
+constexpr int kTileFloats = kBM * kBN;  // one float32 partial tile
+constexpr int kMaxSplit = 8;
+
+// Workgroup b runs tile b whole if b < full; otherwise part (b - full) % split
+// of tail tile full + (b - full) / split, over K steps [k0, k1).
+struct WorkItem {
+  int tile, part, parts, k0, k1;
+  int64_t m0, n0;
+};
+__device__ __forceinline__ WorkItem work_item(int gn, int nk, int full, int split) {
+  WorkItem w;
+  const int b = blockIdx.x;
+  if (b < full) {
+    w.tile = b;
+    w.part = 0;
+    w.parts = 1;
+    w.k0 = 0;
+    w.k1 = nk;
+  } else {
+    const int p = b - full;
+    w.tile = full + p / split;
+    w.part = p % split;
+    w.parts = split;
+    w.k0 = w.part * nk / split;
+    w.k1 = (w.part + 1) * nk / split;
+  }
+  w.m0 = (int64_t)(w.tile / gn) * kBM;
+  w.n0 = (int64_t)(w.tile % gn) * kBN;
+  return w;
+}
+
+// End of a K part of a tail tile. Every part stores its float32 tile
+// (device-scope stores, written through to memory), counts itself in, and
+// waits (bounded) until all parts of the tile have; then part p sums row
+// tiles [8p/parts, 8(p+1)/parts) of all parts, in part order (device-scope
+// loads; the sum does not depend on which part finished first), and stages
+// those rows as bf16 for the caller to store. A second count lets the last
+// part out reset the counter for the next launch. Wave w's accumulators sit
+// at floats [16384 w, 16384 (w+1)) of a part's tile as 64 chunks of 1 KB,
+// lane-major. The parts of a tile are consecutive workgroups: when they do not
+// all fit on the chip at once, the ones waiting hold their compute units only
+// until the earlier tiles' parts finish. A wait that runs out sets the
+// workspace's error word and goes on (the tile is then wrong, nothing hangs).
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ void split_combine(const f32x16 (&acc)[8][2], float *tile_parts, int part, int parts,
+                                              uint32_t *counter, uint32_t *err, uint16_t *stage, int tid, int wave,
+                                              int lane) {
+  const rsrc_t pr = make_rsrc(tile_parts, (int64_t)parts * kTileFloats * 4);
+  const uint32_t lane_off = (uint32_t)(wave * (kTileFloats / 4) + 4 * lane) * 4u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const u32x4 v = {__float_as_uint(acc[i][j][4 * e4]), __float_as_uint(acc[i][j][4 * e4 + 1]),
+                         __float_as_uint(acc[i][j][4 * e4 + 2]), __float_as_uint(acc[i][j][4 * e4 + 3])};
+        const uint32_t off = (uint32_t)(part * kTileFloats) * 4u + lane_off + (uint32_t)((i * 2 + j) * 4 + e4) * 1024u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, pr, off, 0, 16);
+      }
+  wait_barrier<0>();  // every wave's stores have completed
+  if (tid == 0) {
+    add_dev_u32(counter, 1u);
+    int it = 0;
+    while (ld_dev_u32(counter) < (uint32_t)parts) {
+      if (++it >= kSpinLimit) {
+        st_dev_u32(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  wait_barrier<0>();
+  const int ilo = part * 8 / parts, ihi = (part + 1) * 8 / parts;
+  for (int i = ilo; i < ihi; ++i) {
+    f32x4 sum[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) sum[j][e4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < parts; ++p) {
+      u32x4 v[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          v[j][e4] = bld16_dev(pr, (uint32_t)(p * kTileFloats) * 4u + lane_off + (uint32_t)((i * 2 + j) * 4 + e4) * 1024u);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sum[j][e4][u] += __uint_as_float(v[j][e4][u]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        stage_put4(stage, lane, i, j, e4, sum[j][e4][0], sum[j][e4][1], sum[j][e4][2], sum[j][e4][3]);
+  }
+  wait_vmem();
+  if (tid == 0 && add_dev_u32(counter, 1u) == (uint32_t)(2 * parts - 1)) st_dev_u32(counter, 0u);
 }
-
-// Activation chunk i (< 4) of lane `tid`: row (tid + 512 i) / 8, columns 8 ((tid + 512 i) % 8) .. + 7.
-__device__ __forceinline__ int act_row(int tid, int i) { return (tid + kThreads * i) >> 3; }
-__device__ __forceinline__ int act_col(int tid) { return (tid & 7) * 8; }
 
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-constexpr size_t kFwdTiles = (size_t)2 * (kBM + kBN) * kAP * sizeof(uint16_t);
-constexpr size_t kFwdLds = kFwdTiles > kStageLds ? kFwdTiles : kStageLds;
+// Codes of one K step held by one lane: for each of its two output rows
+// (column tiles j = 0, 1) the four code words of its K half, the block's scale
+// code and its group maximum.
+struct FwdCodes {
+  u32x4 c[2];
+  uint32_t q2[2];
+  float S[2];
+};
 
 __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ qscale,
@@ -215,16 +443,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
                                                        const uint16_t *__restrict__ x, int64_t T,
                                                        const uint16_t *__restrict__ su, int r_pad,
                                                        const uint16_t *__restrict__ B, int r,
-                                                       uint16_t *__restrict__ h) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t *As = smem;                        // [2][kBM][kAP]  x tile [t][k]
-  uint16_t *Bs = smem + 2 * kBM * kAP;        // [2][kBN][kAP]  W_hat tile [n][k]
+                                                       uint16_t *__restrict__ h, float *__restrict__ partial,
+                                                       uint32_t *__restrict__ counters, int gn, int full,
+                                                       int split) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [2][kTile] activation ring
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int half = lane >> 5, ml = lane & 31;
   const int64_t KB = d_in / kBlock;
   const int nk = (int)KB;
-  const int nk_lora = r > 0 ? (r_pad + kBK - 1) / kBK : 0;
+  const WorkItem wi = work_item(gn, nk, full, split);
+  const int64_t m0 = wi.m0, n0 = wi.n0;
+  const int k0 = wi.k0, k1 = wi.k1;
+  const int nk_lora = r > 0 && wi.part == wi.parts - 1 ? (r_pad + kBK - 1) / kBK : 0;
 
   // Buffer ranges of this tile (rows past T / d_out read zeros).
   const int64_t mrows = T - m0 < kBM ? T - m0 : kBM;
@@ -234,92 +464,175 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   const rsrc_t qr = make_rsrc(qscale + n0 * KB, nrows * KB);
   const rsrc_t sr = make_rsrc(smax, ((d_out * KB + kGroup - 1) / kGroup) * 4);
 
-  const int wrow = tid >> 1, half = tid & 1;  // weight: tile row tid/2, half tid%2 of its block
-  const int ac = act_col(tid);
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = a_off(lane, s);
+  const DmaOffs xo = dma_offsets((int)d_in, wave, lane);
 
-  auto issue = [&](int kt, TileRegs &R) {
-    const bool in = kt < nk;  // tiles past the end read zeros
-    const int64_t k0 = (int64_t)kt * kBK;
+  // This lane's output rows (column tiles j = 0, 1) within the tile: byte
+  // offsets of their code rows and scale-code rows, and their first block index.
+  uint32_t coff[2], qoff[2], blk0[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.a[i] = bld16(xr, in ? (uint32_t)((act_row(tid, i) * d_in + k0 + ac) * 2) : kOOB);
-    R.c = bld16(cr, in ? (uint32_t)(wrow * (d_in / 2) + (int64_t)kt * (kBlock / 2) + 16 * half) : kOOB);
-    R.q2 = bld8(qr, in ? (uint32_t)(wrow * KB + kt) : kOOB);
-    R.S = __uint_as_float(bld32(sr, in ? (uint32_t)((((n0 + wrow) * KB + kt) >> 8) * 4) : kOOB));
-  };
-  auto dsts = [&](int buf, uint16_t *(&adst)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) adst[i] = As + buf * kBM * kAP + act_row(tid, i) * kAP + ac;
-    return Bs + buf * kBN * kAP + wrow * kAP + 32 * half;
-  };
-  struct Frags {
-    const uint16_t *as, *bs;  // this lane's fragment rows in buffer 0
-    __device__ __forceinline__ u32x4 a(int buf, int k16, int i) const {
-      return *reinterpret_cast<const u32x4 *>(as + buf * kBM * kAP + i * 32 * kAP + 16 * k16);
-    }
-    __device__ __forceinline__ void a_all(int buf, int k16, u32x4 (&f)[4]) const {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = a(buf, k16, i);
-    }
-    __device__ __forceinline__ void b(int buf, int k16, u32x4 (&f)[2]) const {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        f[j] = *reinterpret_cast<const u32x4 *>(bs + buf * kBN * kAP + j * 32 * kAP + 16 * k16);
-    }
-  };
-  const Frags frags{As + (wm * kWM + (lane & 31)) * kAP + 8 * (lane >> 5),
-                    Bs + (wn * kWN + (lane & 31)) * kAP + 8 * (lane >> 5)};
-
-  f32x16 acc[4][2];
-  zero_acc(acc);
-
-  // Main K loop: tile kt in LDS buffer kt&1, tile kt+1 in registers, tile kt+2 in flight.
-  TileRegs R0, R1;
-  uint16_t *adst[4];
-  issue(0, R0);
-  issue(1, R1);
-  restore_all(R0, dsts(0, adst), adst);
-  lds_barrier();
-  for (int kt = 0; kt < nk; kt += 2) {
-    issue(kt + 2, R0);
-    k_step(acc, frags, 0, R1, dsts(1, adst), adst);
-    lds_barrier();
-    issue(kt + 3, R1);
-    k_step(acc, frags, 1, R0, dsts(0, adst), adst);
-    lds_barrier();
+  for (int j = 0; j < 2; ++j) {
+    const int row = kWN * wave + 32 * j + ml;
+    coff[j] = (uint32_t)(row * (d_in / 2)) + 16u * half;
+    qoff[j] = (uint32_t)(row * KB);
+    blk0[j] = (uint32_t)((n0 + row) * KB);
   }
-  // (an odd K count ran one zero tile through buffer 1)
+  auto issue_codes = [&](int kt, FwdCodes &C) {
+    const int kc = kt < nk ? kt : nk - 1;  // steps past the end reload the last one (never used)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      C.c[j] = bld16s(cr, coff[j], kc * (kBlock / 2));
+      C.q2[j] = bld8s(qr, qoff[j], kc);
+      C.S[j] = __uint_as_float(bld32(sr, ((blk0[j] + (uint32_t)kc) >> 8) * 4u));
+    }
+  };
 
-  // Adapter K tile(s): su [T, r_pad] and B [d_out, r], both K-contiguous bf16.
+  f32x16 acc[8][2];
+  zero_acc(acc);
+  FwdCodes C0, C1;
+  Nf4Planes t[2];
+  u32x4 fa[2][8], fb[2][2];
+
+  // Prologue: tile 0 in LDS, codes of steps 0 and 1 requested, tables and
+  // fragments of step 0, slice 0 ready.
+  dma_tile(xr, xo, k0 * kBK, smem, wave);
+  issue_codes(k0, C0);
+  issue_codes(k0 + 1, C1);
+  wait_barrier<6>();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    TableBuild tb;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j], C0.S[j], t[j]);
+    fb[0][j] = expand8(t[j], C0.c[j][0]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fa[0][i] = *reinterpret_cast<const u32x4 *>(smem + aoff[0] + 4096 * i);
+
+  // One K step. Tile kt is in ring slot P = kt & 1, its codes in Ccur; Cnext
+  // holds the codes of step kt+1. Side work after MFMA q of slice s:
+  //   s < 3 : A fragments of slice s+1 (q < 8); B fragments of slice s+1
+  //           (expand pieces at odd q: column tile 0 at q = 1..7, 1 at 9..15);
+  //   s = 3 : codes of step kt+2 into Ccur (q = 0); tables of step kt+1
+  //           (q = 1..6); wait for tile kt+1 and barrier (q = 7); then the
+  //           A and B fragments of step kt+1, slice 0 (q = 8..15).
+  auto step = [&](int kt, const int P, FwdCodes &Ccur, FwdCodes &Cnext) {
+    // (the last step copies its own tile again into the idle slot: no branch)
+    dma_tile(xr, xo, (kt + 1 < k1 ? kt + 1 : kt) * kBK, smem + (P ^ 1) * kTile, wave);
+    const uint8_t *cur = smem + P * kTile, *nxt = smem + (P ^ 1) * kTile;
+    Expand ex;
+    TableBuild tb;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 1, j = q & 1;
+        acc[i][j] = mfma32(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+        QLORA_SCHED_FENCE();
+        if (s < 3) {
+          if (q < 8) fa[(s + 1) & 1][q] = *reinterpret_cast<const u32x4 *>(cur + aoff[s + 1] + 4096 * q);
+          if (q & 1) {
+            const int jj = q >> 3, ph = (q >> 1) & 3;
+            ex.run(ph, t[jj], Ccur.c[jj][s + 1], fb[(s + 1) & 1][jj]);
+          }
+        } else {
+          if (q == 0) issue_codes(kt + 2, Ccur);
+          if (q >= 1 && q <= 6) {
+            const int jj = (q - 1) / 3;
+            tb.run((q - 1) % 3, Cnext.q2[jj], Cnext.S[jj], t[jj]);
+          }
+          if (q == 7) wait_barrier<6>();
+          if (q >= 8) {
+            fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
+            const int jj = (q - 8) >> 2, ph = (q - 8) & 3;
+            ex.run(ph, t[jj], Cnext.c[jj][0], fb[0][jj]);
+          }
+        }
+        QLORA_SCHED_FENCE();
+      }
+    }
+  };
+
+  // Two steps per iteration (the register sets trade roles), no branch between them.
+  int kt = k0;
+  for (; kt + 1 < k1; kt += 2) {
+    step(kt, 0, C0, C1);
+    step(kt + 1, 1, C1, C0);
+  }
+  if (kt < k1) step(kt, 0, C0, C1);
+
+  // Adapter K tile(s) (with the last K part of a split tile): su [T, r_pad] through LDS; B [d_out, r] fragments
+  // straight from memory (lane: row of its column tile, K 32h + 8s .. +7).
   const rsrc_t ur = make_rsrc(su + m0 * r_pad, mrows * r_pad * 2);
   const rsrc_t br = make_rsrc(B + n0 * r, nrows * r * 2);
   for (int lt = 0; lt < nk_lora; ++lt) {
     const int j0 = lt * kBK;
+    wait_barrier<0>();  // every wave is done with the ring
+    dma_any(ur, dma_offsets(r_pad, wave, lane), j0, r_pad, smem, wave, lane);
+    wait_barrier<0>();
+    plain_tile(acc, smem, aoff, [&](int s, u32x4 (&b)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = act_row(tid, i);
-      const uint32_t off = j0 + ac < r_pad ? (uint32_t)((row * r_pad + j0 + ac) * 2) : kOOB;
-      st16(As + row * kAP + ac, bld16(ur, off));
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = 32 * half + 8 * q;
-      const uint32_t off = j0 + col < r ? (uint32_t)((wrow * r + j0 + col) * 2) : kOOB;
-      st16(Bs + wrow * kAP + col, bld16(br, off));
-    }
-    lds_barrier();
-    k_plain(acc, frags);
-    lds_barrier();
+      for (int j = 0; j < 2; ++j) {
+        const int row = kWN * wave + 32 * j + ml, col = j0 + 32 * half + 8 * s;
+        b[j] = bld16(br, col < r ? (uint32_t)((row * r + col) * 2) : kOOB);
+      }
+    });
   }
 
-  // Epilogue through LDS (the tile buffers are free now).
-  store_tile_bf16(acc, smem + wave * kWM * kEP, lane, h, d_out, m0 + wm * kWM, n0 + wn * kWN, T, d_out);
+  // Epilogue through LDS once every wave is done with the ring.
+  wait_barrier<0>();
+  uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * kBM * kEP;
+  int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
+  if (wi.parts > 1) {
+    split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
+                  counters + (wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
+    rlo = 32 * (wi.part * 8 / wi.parts);
+    rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
+  } else {
+    stage_acc(acc, stage, lane);
+  }
+  stage_store(stage, lane, h, d_out, m0, n0 + kWN * wave, T, d_out, rlo, rhi);
 }
 
 // ---------------------------------------------------------------------------
 // Backward dX
 // ---------------------------------------------------------------------------
-constexpr size_t kDxTiles = (size_t)2 * (kBM * kAP + kBK * kBTP) * sizeof(uint16_t);
-constexpr size_t kDxLds = kDxTiles > kStageLds ? kDxTiles : kStageLds;
+// Codes of one weight block (one lane's share of a 64 x 256 weight tile).
+struct DxCodes {
+  u32x4 c0, c1;
+  uint32_t q2;
+  float S;
+};
+
+// dX weight tiles in LDS: row o (0..63) takes 512 bytes; its 16-byte chunk c
+// (columns 8c .. 8c+7) sits at chunk position c ^ wswz(o). With this swizzle
+// the restore stores (16 lanes: 8 rows x 2 blocks, one chunk each) and the
+// transposed fragment reads (32 lanes: 4 rows x 4 chunks, 8 bytes each) both
+// land on 64 distinct banks.
+__device__ __forceinline__ int wswz(int o) { return ((o & 3) << 2) | ((o >> 1) & 3); }
+
+// Restore of one block into a weight tile in 3 + 32 pieces: table, then per
+// code word the four expand pieces, the last of which stores the 8 weights.
+// Word m of the block goes to byte (wxor ^ 16 m) of the tile: the block's
+// chunks are 8 consecutive positions whose order the swizzle permutes.
+struct DxRestore {
+  TableBuild tb;
+  Nf4Planes t;
+  Expand ex;
+  u32x4 v;
+  __device__ __forceinline__ void run(int k, const DxCodes &C, uint8_t *tile, uint32_t wxor) {
+    if (k < 3) {
+      tb.run(k, C.q2, C.S, t);
+    } else if (k < 35) {
+      const int m = (k - 3) >> 2, ph = (k - 3) & 3;
+      const uint32_t w = m < 4 ? C.c0[m & 3] : C.c1[m & 3];
+      ex.run(ph, t, w, v);
+      if (ph == 3) st16(tile + (wxor ^ (16u * m)), v);
+    }
+  }
+};
 
 __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ qscale,
@@ -327,127 +640,176 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
                                                       const uint16_t *__restrict__ dY, int64_t T,
                                                       const uint16_t *__restrict__ sv, int r_pad,
                                                       const uint16_t *__restrict__ A, int r,
-                                                      uint16_t *__restrict__ dX) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t *As = smem;                      // [2][kBM][kAP]   dY tile [t][o]
-  uint16_t *Bt = smem + 2 * kBM * kAP;      // [2][kBK][kBTP]  W_hat tile [o][i]
+                                                      uint16_t *__restrict__ dX, float *__restrict__ partial,
+                                                      uint32_t *__restrict__ counters, int gn, int full,
+                                                      int split) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t *ring = smem;                                             // [2][kTile]     dY tiles [t][o]
+  uint8_t *Bt = smem + 2 * kTile;                                   // [2][kWTile]    W_hat tiles [o][i]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;  // n = input feature i
   const int64_t KB = d_in / kBlock;
   const int nk = (int)((d_out + kBK - 1) / kBK);
-  const int nk_lora = r > 0 ? (r_pad + kBK - 1) / kBK : 0;
+  const WorkItem wi = work_item(gn, nk, full, split);
+  const int64_t m0 = wi.m0, n0 = wi.n0;  // n = input feature i
+  const int k0 = wi.k0, k1 = wi.k1;
+  const int nk_lora = r > 0 && wi.part == wi.parts - 1 ? (r_pad + kBK - 1) / kBK : 0;
 
   const int64_t mrows = T - m0 < kBM ? T - m0 : kBM;
-  const rsrc_t yr = make_rsrc(dY + m0 * d_out, mrows * d_out * 2);
+  const i32x4 yr = rsrc_words(dY + m0 * d_out, mrows * d_out * 2);
+  const DmaOffs yo = dma_offsets((int)d_out, wave, lane);
 
-  const int ac = act_col(tid);
-  // weight tile: 64 rows o x 4 blocks of 64 columns i; lane -> block tid/2 (row wo, block wb), half tid%2
-  const int wblk = tid >> 1, half = tid & 1;
-  const int wo = wblk >> 2, wb = wblk & 3;
-  const int64_t kblk = n0 / kBlock + wb;
-
-  auto issue = [&](int kt, TileRegs &R) {
-    const int64_t k0 = (int64_t)kt * kBK;
-    const bool aok = kt < nk && k0 + ac < d_out;
+  int aoff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.a[i] = bld16(yr, aok ? (uint32_t)((act_row(tid, i) * d_out + k0 + ac) * 2) : kOOB);
+  for (int s = 0; s < 4; ++s) aoff[s] = a_off(lane, s);
+  // B fragment of column tile j, slice s from a weight tile: lane gets column
+  // 64w + 32j + l%32, K rows 32h + 8s .. +7. Within each 16 lanes
+  // ds_read_b64_tr_b16 hands lane u element e of the 8 bytes that lane
+  // 4e + u/4 addresses (its 16-bit element u%4); lane u of group g therefore
+  // addresses K row 32(g/2) + 8s + u/4, columns 16(g%2) + 4(u%4) .. +3, and a
+  // second read four rows further down gives elements 4..7. Row o mod 8 does
+  // not depend on s, so the swizzled byte offsets (per j, per half) are fixed
+  // per lane and slices add 4096 s.
+  const int grp = lane >> 4, u16 = lane & 15;
+  uint32_t boff[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 32 * (grp >> 1) + (u16 >> 2) + 4 * hh;
+      const int col = kWN * wave + 32 * j + 16 * (grp & 1) + 4 * (u16 & 3);
+      boff[j][hh] = (uint32_t)(row * kWRow + (((col >> 3) ^ wswz(row)) << 4) + (col & 7) * 2);
+    }
+  auto frag_b = [&](const uint8_t *bt, int s, int j) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(bt + boff[j][0] + 4096 * s));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(bt + boff[j][1] + 4096 * s));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+
+  // weight tile: 64 rows o x 4 blocks of 64 columns i; lanes 16G + u take row
+  // 8 (G % 8) + u % 8, block 2 (G / 8) + u / 8 (8 rows x 2 blocks per 16 lanes)
+  const int wo = 8 * ((tid >> 4) & 7) + (tid & 7), wb = 2 * (tid >> 7) + ((tid >> 3) & 1);
+  const uint32_t wxor = (uint32_t)(wo * kWRow + ((8 * wb ^ wswz(wo)) << 4));
+  const int64_t kblk = n0 / kBlock + wb;
+  auto issue_codes = [&](int kt, DxCodes &C) {
     // weight rows k0..k0+63: ranges rebased per K tile (32-bit offsets stay small for any weight size)
+    const int64_t k0 = (int64_t)kt * kBK;
     const int64_t orows = kt < nk ? (d_out - k0 < kBK ? d_out - k0 : kBK) : 0;
     const int64_t kr = kt < nk ? k0 : 0;
-    const rsrc_t cr = make_rsrc(codes + kr * (d_in / 2), orows * (d_in / 2));
-    const rsrc_t qr = make_rsrc(qscale + kr * KB, orows * KB);
+    const rsrc_t crr = make_rsrc(codes + kr * (d_in / 2), orows * (d_in / 2));
+    const rsrc_t qrr = make_rsrc(qscale + kr * KB, orows * KB);
     const int64_t gb = (kr * KB) >> 8;  // first group of the tile's rows
-    const rsrc_t sr = make_rsrc(smax + gb, ((d_out * KB + kGroup - 1) / kGroup - gb) * 4);
+    const rsrc_t srr = make_rsrc(smax + gb, ((d_out * KB + kGroup - 1) / kGroup - gb) * 4);
     // Rows past the tile's end fall outside the ranges and restore to zero
     // (scale code 0). Blocks past d_in (kblk >= KB) read the next row's
     // blocks: finite values that reach only output columns past d_in, which
     // are never stored.
     const uint32_t lblk = (uint32_t)(wo * KB + kblk);  // block index within the tile
-    R.c = bld16(cr, lblk * 32u + 16u * half);
-    R.q2 = bld8(qr, lblk);
-    R.S = __uint_as_float(bld32(sr, (uint32_t)((((kr * KB) & (kGroup - 1)) + lblk) >> 8) * 4u));
+    C.c0 = bld16(crr, lblk * 32u);
+    C.c1 = bld16(crr, lblk * 32u + 16u);
+    C.q2 = bld8(qrr, lblk);
+    C.S = __uint_as_float(bld32(srr, (uint32_t)((((kr * KB) & (kGroup - 1)) + lblk) >> 8) * 4u));
   };
-  auto dsts = [&](int buf, uint16_t *(&adst)[4]) {
+
+  f32x16 acc[8][2];
+  zero_acc(acc);
+  DxCodes C0, C1;
+  u32x4 fa[2][8], fb[2][2];
+
+  // Prologue: dY tile 0 and weight tile 0 in LDS, codes of step 1 requested,
+  // fragments of step 0, slice 0 ready.
+  dma_tile_asm(yr, yo, k0 * kBK, (int)d_out, ring, wave, lane);
+  issue_codes(k0, C0);
+  issue_codes(k0 + 1, C1);
+  {
+    DxRestore rs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) adst[i] = As + buf * kBM * kAP + act_row(tid, i) * kAP + ac;
-    return Bt + buf * kBK * kBTP + wo * kBTP + wb * 64 + 32 * half;
-  };
-  struct Frags {
-    const uint16_t *as;  // this lane's A fragment rows in buffer 0
-    const uint16_t *bt;  // the address this lane hands to the transposed reads of column tile 0, slice 0, buffer 0
-    __device__ __forceinline__ u32x4 a(int buf, int k16, int i) const {
-      return *reinterpret_cast<const u32x4 *>(as + buf * kBM * kAP + i * 32 * kAP + 16 * k16);
-    }
-    __device__ __forceinline__ void a_all(int buf, int k16, u32x4 (&f)[4]) const {
+    for (int k = 0; k < 35; ++k) rs.run(k, C0, Bt, wxor);
+  }
+  wait_barrier<4>();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = a(buf, k16, i);
-    }
-    __device__ __forceinline__ void b(int buf, int k16, u32x4 (&f)[2]) const {
-      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  for (int i = 0; i < 8; ++i) fa[0][i] = *reinterpret_cast<const u32x4 *>(ring + aoff[0] + 4096 * i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint16_t *t = bt + buf * kBK * kBTP + 16 * k16 * kBTP + 32 * j;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)t);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(t + 4 * kBTP));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        f[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  for (int j = 0; j < 2; ++j) fb[0][j] = frag_b(Bt, 0, j);
+
+  // One K step. Tiles of step kt are in slot P; Cnext holds the codes of step
+  // kt+1, whose weight tile is restored into slot P^1 during this step; Ccur
+  // (dead) receives the codes of step kt+2. Side work after MFMA q of slice s:
+  //   s < 3 : A fragments of slice s+1 (q < 8), B fragments (q = 8, 10);
+  //           restore pieces 16s + q (all 35 done within slice 2);
+  //   s = 3 : wait for the copies and stores of step kt+1 and barrier (q = 7);
+  //           A and B fragments of step kt+1, slice 0 (q = 8..15).
+  auto step = [&](int kt, const int P, DxCodes &Ccur, DxCodes &Cnext) {
+    wait_vmem();  // codes of step kt+1 (requested a step ago) are in; see dma16_asm
+    dma_tile_asm(yr, yo, (kt + 1 < k1 ? kt + 1 : kt) * kBK, (int)d_out, ring + (P ^ 1) * kTile, wave, lane);
+    issue_codes(kt + 2, Ccur);
+    const uint8_t *cur = ring + P * kTile, *nxt = ring + (P ^ 1) * kTile;
+    const uint8_t *bcur = Bt + P * kWTile;
+    uint8_t *bnxt = Bt + (P ^ 1) * kWTile;
+    DxRestore rs;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 1, j = q & 1;
+        acc[i][j] = mfma32(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+        QLORA_SCHED_FENCE();
+        if (s < 3) {
+          if (q < 8) fa[(s + 1) & 1][q] = *reinterpret_cast<const u32x4 *>(cur + aoff[s + 1] + 4096 * q);
+          if (q == 8 || q == 10) fb[(s + 1) & 1][(q - 8) >> 1] = frag_b(bcur, s + 1, (q - 8) >> 1);
+          rs.run(16 * s + q, Cnext, bnxt, wxor);
+        } else {
+          if (q == 7) wait_barrier<4>();
+          if (q >= 8) fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
+          if (q == 12 || q == 14) fb[0][(q - 12) >> 1] = frag_b(bnxt, 0, (q - 12) >> 1);
+        }
+        QLORA_SCHED_FENCE();
       }
     }
   };
-  // B fragment of v_mfma_f32_32x32x16_bf16 from the [k][n] weight tile: lane l
-  // gets column n + l%32, rows k0 + 8(l/32) .. + 7. Within each 16 lanes,
-  // ds_read_b64_tr_b16 hands lane j element e of the 8 bytes that lane
-  // 4e + j/4 addresses (its 16-bit element j%4); lane s of group g therefore
-  // addresses row 8(g/2) + s/4, columns 16(g%2) + 4(s%4) .. + 3, and a second
-  // read four rows further down gives elements 4..7.
-  const int tgrp = lane >> 4, ts = lane & 15;
-  const Frags frags{As + (wm * kWM + (lane & 31)) * kAP + 8 * (lane >> 5),
-                    Bt + (8 * (tgrp >> 1) + (ts >> 2)) * kBTP + wn * kWN + 16 * (tgrp & 1) + 4 * (ts & 3)};
 
-  f32x16 acc[4][2];
-  zero_acc(acc);
-
-  TileRegs R0, R1;
-  uint16_t *adst[4];
-  issue(0, R0);
-  issue(1, R1);
-  restore_all(R0, dsts(0, adst), adst);
-  lds_barrier();
-  for (int kt = 0; kt < nk; kt += 2) {
-    issue(kt + 2, R0);
-    k_step(acc, frags, 0, R1, dsts(1, adst), adst);
-    lds_barrier();
-    issue(kt + 3, R1);
-    k_step(acc, frags, 1, R0, dsts(0, adst), adst);
-    lds_barrier();
+  // Two steps per iteration (the register sets trade roles), no branch between them.
+  int kt = k0;
+  for (; kt + 1 < k1; kt += 2) {
+    step(kt, 0, C0, C1);
+    step(kt + 1, 1, C1, C0);
   }
+  if (kt < k1) step(kt, 0, C0, C1);
 
-  const rsrc_t vr = make_rsrc(sv + m0 * r_pad, mrows * r_pad * 2);
   const rsrc_t ar = make_rsrc(A, (int64_t)r * d_in * 2);
   for (int lt = 0; lt < nk_lora; ++lt) {
     const int j0 = lt * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = act_row(tid, i);
-      const uint32_t off = j0 + ac < r_pad ? (uint32_t)((row * r_pad + j0 + ac) * 2) : kOOB;
-      st16(As + row * kAP + ac, bld16(vr, off));
-    }
-    // A rows j0..j0+63, columns n0..n0+255
+    wait_barrier<0>();  // every wave is done with the ring and the weight tiles
+    dma_tile_asm(rsrc_words(sv + m0 * r_pad, mrows * r_pad * 2), dma_offsets(r_pad, wave, lane), j0, r_pad, ring,
+                 wave, lane);
+    // A rows j0..j0+63, columns n0..n0+255 -> weight tile slot 0
 #pragma unroll
     for (int q = 0; q < kBK * (kBN / 8) / kThreads; ++q) {
       const int e = q * kThreads + tid;
       const int jr = e / (kBN / 8), cc = (e % (kBN / 8)) * 8;
-      const int64_t j = j0 + jr, i = n0 + cc;
-      const uint32_t off = (j < r && i < d_in) ? (uint32_t)((j * d_in + i) * 2) : kOOB;
-      st16(Bt + jr * kBTP + cc, bld16(ar, off));
+      const int64_t jj = j0 + jr, ii = n0 + cc;
+      const uint32_t off = (jj < r && ii < d_in) ? (uint32_t)((jj * d_in + ii) * 2) : kOOB;
+      st16(Bt + jr * kWRow + ((((cc >> 3) ^ wswz(jr))) << 4), bld16(ar, off));
     }
-    lds_barrier();
-    k_plain(acc, frags);
-    lds_barrier();
+    wait_barrier<0>();
+    plain_tile(acc, ring, aoff, [&](int s, u32x4 (&b)[2]) {
+      b[0] = frag_b(Bt, s, 0);
+      b[1] = frag_b(Bt, s, 1);
+    });
   }
 
-  store_tile_bf16(acc, smem + wave * kWM * kEP, lane, dX, d_in, m0 + wm * kWM, n0 + wn * kWN, T, d_in);
+  wait_barrier<0>();
+  uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * kBM * kEP;
+  int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
+  if (wi.parts > 1) {
+    split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
+                  counters + (wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
+    rlo = 32 * (wi.part * 8 / wi.parts);
+    rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
+  } else {
+    stage_acc(acc, stage, lane);
+  }
+  stage_store(stage, lane, dX, d_in, m0, n0 + kWN * wave, T, d_in, rlo, rhi);
 }
 
 static bool g_attr_set[64];
@@ -466,25 +828,73 @@ static hipError_t set_lds_attrs() {
   return hipSuccess;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Choose the K split of the tail tiles by a step count: whole tiles take nk
+// steps per round of `cus` tiles; a round of parts takes ceil(nk/s) steps plus
+// a fixed cost (prologue and epilogue of a short K range, storing a float32
+// partial tile, waiting for the other parts and reading back a 1/s share of
+// all of them), measured at about 24 steps.
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t nk) {
+  GemmPlan p{};
+  p.gm = (int)((M + kBM - 1) / kBM);
+  p.gn = (int)((N + kBN - 1) / kBN);
+  p.nk = (int)nk;
+  const int64_t tiles = (int64_t)p.gm * p.gn, cus = device_cus();
+  const int64_t rounds = tiles / cus, rem = tiles % cus;
+  int best = 1;
+  int64_t best_cost = rounds * nk + (rem > 0 ? nk : 0);
+  for (int s = 2; s <= kMaxSplit && s <= nk && rem > 0; ++s) {
+    const int64_t cost = rounds * nk + (rem * s + cus - 1) / cus * ((nk + s - 1) / s + 24);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  p.split = best;
+  p.rem = best > 1 ? (int)rem : 0;
+  p.full = (int)(tiles - p.rem);
+  return p;
+}
+
+size_t gemm_partial_floats(const GemmPlan &p) { return (size_t)p.rem * p.split * kTileFloats; }
+
 hipError_t launch_gemm_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *su, int r_pad,
-                           const uint16_t *B, int r, uint16_t *h, const Nf4Consts &c, hipStream_t st) {
-  (void)c;
+                           const uint16_t *B, int r, uint16_t *h, float *partial, uint32_t *counters,
+                           hipStream_t st) {
   hipError_t e = set_lds_attrs();
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((d_out + kBN - 1) / kBN), (unsigned)((T + kBM - 1) / kBM));
-  k_gemm_fwd<<<grid, dim3(kThreads), kFwdLds, st>>>(codes, qscale, smax, d_out, d_in, x, T, su, r_pad, B, r, h);
+  const GemmPlan p = gemm_plan(T, d_out, d_in / kBlock);
+  if (p.rem > kMaxTileCounters) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(p.full + p.rem * p.split);
+  k_gemm_fwd<<<dim3(grid), dim3(kThreads), kFwdLds, st>>>(codes, qscale, smax, d_out, d_in, x, T, su, r_pad, B, r,
+                                                            h, partial, counters, p.gn, p.full, p.split);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dx(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                           int64_t d_in, const uint16_t *dY, int64_t T, const uint16_t *sv, int r_pad,
-                          const uint16_t *A, int r, uint16_t *dX, const Nf4Consts &c, hipStream_t st) {
-  (void)c;
+                          const uint16_t *A, int r, uint16_t *dX, float *partial, uint32_t *counters,
+                          hipStream_t st) {
   hipError_t e = set_lds_attrs();
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((d_in + kBN - 1) / kBN), (unsigned)((T + kBM - 1) / kBM));
-  k_gemm_dx<<<grid, dim3(kThreads), kDxLds, st>>>(codes, qscale, smax, d_out, d_in, dY, T, sv, r_pad, A, r, dX);
+  const GemmPlan p = gemm_plan(T, d_in, (d_out + kBK - 1) / kBK);
+  if (p.rem > kMaxTileCounters) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(p.full + p.rem * p.split);
+  k_gemm_dx<<<dim3(grid), dim3(kThreads), kDxLds, st>>>(codes, qscale, smax, d_out, d_in, dY, T, sv, r_pad, A, r,
+                                                          dX, partial, counters, p.gn, p.full, p.split);
   return hipGetLastError();
 }
 

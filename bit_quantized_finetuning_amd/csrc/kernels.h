@@ -41,13 +41,27 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
 bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T);
 
 // gemm.hip: T > 16 (and any T the weight-streaming kernel does not take).
+// Work split of one contraction over 256 x 256 output tiles (gm x gn of them,
+// nk K steps of 64 each): tiles 0 .. full-1 run whole, one workgroup each; each
+// of the remaining `rem` tiles is cut into `split` K ranges run by separate
+// workgroups, whose float32 partial tiles (gemm_partial_floats in total, in
+// the workspace's shared scratch region) are summed by the last range to
+// finish. Chosen so that the chip's last round of tiles is not left mostly
+// idle; depends on the current device's compute-unit count.
+struct GemmPlan {
+  int gm, gn, nk, full, rem, split;
+};
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t nk);
+size_t gemm_partial_floats(const GemmPlan &p);
 hipError_t launch_gemm_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *su, int r_pad,
-                           const uint16_t *B, int r, uint16_t *h, const Nf4Consts &c, hipStream_t st);
+                           const uint16_t *B, int r, uint16_t *h, float *partial, uint32_t *counters,
+                           hipStream_t st);
 // dX[T, d_in] = dY W_hat + sv A (sv = bf16(s*v) [T, r_pad], A [r, d_in]).
 hipError_t launch_gemm_dx(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                           int64_t d_in, const uint16_t *dY, int64_t T, const uint16_t *sv, int r_pad,
-                          const uint16_t *A, int r, uint16_t *dX, const Nf4Consts &c, hipStream_t st);
+                          const uint16_t *A, int r, uint16_t *dX, float *partial, uint32_t *counters,
+                          hipStream_t st);
 
 // lora_grad.hip: C[M, N] = scale * sum_t P[t, m] Q[t, n] over t < T.
 // P and Q are each bf16 or f32 (an f32 operand is split into two bf16 terms).

@@ -47,10 +47,13 @@ def test_storage_bytes_matches_oracle(shape):
     assert q.qlora_storage_bytes(*shape) == oracle.storage_bytes(*shape)
 
 
-def test_workspace_bytes_positive_and_grows():
+def test_workspace_bytes_positive_and_covers_buffers():
+    # Not monotone in T: a tile count that leaves the last round of compute
+    # units partly idle adds float32 partial tiles of a K split.
     a = q.qlora_workspace_bytes(4096, 4096, 16, 64)
     b = q.qlora_workspace_bytes(4096, 4096, 4096, 64)
-    assert 0 < a < b
+    assert a >= 65536 and b >= 65536
+    assert b >= 65536 + 2 * 4096 * 64 * 4  # counters + float32 u and v at T = 4096
     assert q.qlora_workspace_bytes(4096, 4096, 16, 0) > 0
     assert q.qlora_workspace_bytes(0, 4096, 16, 0) == 0
 
