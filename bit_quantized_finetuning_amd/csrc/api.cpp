@@ -132,10 +132,16 @@ Layout layout(int64_t d_out, int64_t d_in, int64_t T, int r) {
   L.bt = off;
   off = align256(off + (size_t)r * d_out * 2);
   size_t pf = 0;
-  if (r > 0) {
+  if (r > 0 && T < kWideMinTokens) {
     pf = std::max(pf, (size_t)ceil_div(T, 16) * lora_small_ksplit(T, std::max(d_in, d_out)) * 16 * rp);
     pf = std::max(pf, lora_grad_partial_floats(r, d_in, T));
     pf = std::max(pf, lora_grad_partial_floats(d_out, r, T));
+  }
+  if (r > 0 && T >= kWideMinTokens) {
+    pf = std::max(pf, lora_tall_partial_floats(T, d_in, rp));
+    pf = std::max(pf, lora_tall_partial_floats(T, d_out, rp));
+    pf = std::max(pf, lora_wgrad_partial_floats(d_in, r, T));
+    pf = std::max(pf, lora_wgrad_partial_floats(d_out, r, T));
   }
   // K-split tail tiles of the large-T contractions (forward over d_in, dX over d_out)
   pf = std::max(pf, gemm_partial_floats(gemm_plan(T, d_out, d_in / kBlock)));
@@ -239,8 +245,12 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   float *partial = at<float>(ws, L.partial);
   hipError_t e = hipSuccess;
   if (r > 0) {
-    const int ks = lora_small_ksplit(T, d_in);
-    e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
+    if (T >= kWideMinTokens) {
+      e = launch_lora_tall(x, A, T, d_in, r, rp, sc, u_out, su, partial, at<uint32_t>(ws, 0), stream);
+    } else {
+      const int ks = lora_small_ksplit(T, d_in);
+      e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
+    }
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
@@ -284,8 +294,11 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
     uint16_t *bt = at<uint16_t>(ws, L.bt);
     e = launch_transpose_bf16(B, d_out, r, bt, stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
-    e = launch_lora_small(dY, bt, T, d_out, r, sc, v, sv, rp, partial, cnt_small, lora_small_ksplit(T, d_out),
-                          stream);
+    if (T >= kWideMinTokens)
+      e = launch_lora_tall(dY, bt, T, d_out, r, rp, sc, v, sv, partial, cnt_small, stream);
+    else
+      e = launch_lora_small(dY, bt, T, d_out, r, sc, v, sv, rp, partial, cnt_small, lora_small_ksplit(T, d_out),
+                            stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dX) {
@@ -293,21 +306,32 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
                        at<uint32_t>(ws, 0), stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
+  const bool wide = T >= kWideMinTokens;
+  uint32_t *err = at<uint32_t>(ws, (kMaxCounters - 1) * 4);
   if (dA) {
-    e = launch_lora_grad(v, true, r, x, false, d_in, T, sc, dA, partial, at<uint32_t>(ws, 0),
-                         lora_grad_ksplit(r, d_in, T), stream);
+    if (wide)
+      e = launch_lora_wgrad(x, v, T, d_in, r, true, sc, dA, partial, at<uint32_t>(ws, 0), err, stream);
+    else
+      e = launch_lora_grad(v, true, r, x, false, d_in, T, sc, dA, partial, at<uint32_t>(ws, 0),
+                           lora_grad_ksplit(r, d_in, T), stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dB) {
     if (!u) {
       float *uw = at<float>(ws, L.u);
-      e = launch_lora_small(x, A, T, d_in, r, 1.f, uw, nullptr, rp, partial, cnt_small, lora_small_ksplit(T, d_in),
-                            stream);
+      if (wide)
+        e = launch_lora_tall(x, A, T, d_in, r, rp, 1.f, uw, nullptr, partial, cnt_small, stream);
+      else
+        e = launch_lora_small(x, A, T, d_in, r, 1.f, uw, nullptr, rp, partial, cnt_small,
+                              lora_small_ksplit(T, d_in), stream);
       if (e != hipSuccess) return QLORA_ERR_HIP;
       u = uw;
     }
-    e = launch_lora_grad(dY, false, d_out, u, true, r, T, sc, dB, partial, at<uint32_t>(ws, 0),
-                         lora_grad_ksplit(d_out, r, T), stream);
+    if (wide)
+      e = launch_lora_wgrad(dY, u, T, d_out, r, false, sc, dB, partial, at<uint32_t>(ws, 0), err, stream);
+    else
+      e = launch_lora_grad(dY, false, d_out, u, true, r, T, sc, dB, partial, at<uint32_t>(ws, 0),
+                           lora_grad_ksplit(d_out, r, T), stream);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   return QLORA_OK;

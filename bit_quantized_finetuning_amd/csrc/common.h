@@ -20,12 +20,20 @@ constexpr int kBlock = 64;
 constexpr int kGroup = 256;
 // Split reductions count arriving workgroups per output tile in a fixed region
 // at the start of the workspace (zero before first use, left zero by every
-// kernel). A kernel whose tile count exceeds kMaxTileCounters runs without a
-// split. The last kSyncWords words of the region are reserved for the skinny
-// forward; the last of them is set if one of its bounded waits timed out.
+// kernel). Each tile's counter has a 128-byte line of its own: the workgroups
+// of all tiles arrive and poll at about the same time, and counters that share
+// a line serialize at one memory channel (measured: a third of a K-split
+// gradient kernel's time). A kernel whose tile count exceeds kMaxTileCounters
+// runs without a split. The last kSyncWords words of the region are reserved
+// for the skinny forward; the last of them is set if one of its bounded waits
+// timed out.
 constexpr int64_t kMaxCounters = 16384;
 constexpr int64_t kSyncWords = 4;
-constexpr int64_t kMaxTileCounters = kMaxCounters - kSyncWords;
+constexpr int64_t kCounterStride = 32;  // 32-bit words per tile counter
+constexpr int64_t kMaxTileCounters = (kMaxCounters - kSyncWords) / kCounterStride;
+__host__ __device__ inline uint32_t *tile_counter(uint32_t *counters, int64_t tile) {
+  return counters + tile * kCounterStride;
+}
 
 // The 16 NF4 levels as float32 bit patterns, ascending. Kernels that build
 // restore tables take them as literal operands (no registers held across the

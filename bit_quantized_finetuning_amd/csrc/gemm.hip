@@ -38,6 +38,7 @@
 //     slice so that the matrix core keeps working across it.
 // The epilogue goes through LDS so that every lane writes 16-byte rows.
 #include "kernels.h"
+#include "tiles.h"
 
 namespace qlora {
 
@@ -53,30 +54,6 @@ constexpr size_t kFwdTiles = (size_t)2 * kTile;
 constexpr size_t kDxTiles = (size_t)2 * kTile + (size_t)2 * kWTile;
 constexpr size_t kFwdLds = kFwdTiles > kStageLds ? kFwdTiles : kStageLds;
 constexpr size_t kDxLds = kDxTiles > kStageLds ? kDxTiles : kStageLds;
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-#define QLORA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Pin a value to this point of the instruction stream: an empty volatile asm
-// that reads and rewrites it. Scheduling fences order only instructions with
-// side effects; pure arithmetic would otherwise drift to its first use (or up
-// to its inputs). Pinning a piece's inputs before it and its results after it
-// keeps each restore piece between the MFMAs it was written between.
-__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(u32x4 &x) { asm volatile("" : "+v"(x)); }
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// and all of its LDS operations are done, then join the workgroup barrier. One
-// asm block with a memory clobber: no LDS access moves across it, and the
-// copies into LDS still in flight (the newest N operations) are not waited for.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // Activation tiles in LDS: row r (0..255) takes 128 bytes at 128 r; its 16-byte
 // chunk c (K columns 8c .. 8c+7) sits at chunk position c ^ swz(r), which puts
@@ -118,33 +95,6 @@ __device__ __forceinline__ void dma_tile_tail(rsrc_t src, const DmaOffs &o, int 
     const uint32_t off = ((o.v[q] + 2u * (uint32_t)k0) & keep) | (kOOB & ~keep);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void *)(tile + 1024 * (8 * wave + q)), 16, off, 0, 0, 0);
   }
-}
-// The same copies issued from inline asm, for kernels that also read LDS with
-// ds_read_b64_tr_b16: the compiler makes every such read wait for all copies
-// into LDS it knows of, which would stall the first transposed read of a step
-// until the next step's tile has landed. Copies it does not see impose no such
-// wait; the kernel orders them itself (barrier waits with explicit counts) and
-// waits for vmcnt(0) before issuing them, so that the counts the compiler
-// keeps for its own loads never span a copy.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, int64_t bytes) {
-  if (bytes < 0) bytes = 0;
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  const int n = bytes >= 0x7fffffffll ? 0x7fffffff : (int)bytes;
-  // same descriptor as make_rsrc: 48-bit base, stride 0, range n, raw 32-bit format
-  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), n, 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
-}
-__device__ __forceinline__ void dma16_asm(const i32x4 &rs, uint32_t m0v, uint32_t voff, uint32_t soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(m0v), "v"(voff), "s"(rs), "s"(soff)
-      : "memory");  // M0 is reserved (never allocated); nothing else in the kernels that use this reads it
 }
 // Checked copies (chunks at or past klim read zeros) from asm.
 __device__ __forceinline__ void dma_tile_asm(const i32x4 &rs, const DmaOffs &o, int k0, int klim, uint8_t *tile,
@@ -587,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
   if (wi.parts > 1) {
     split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
-                  counters + (wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
+                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
     rlo = 32 * (wi.part * 8 / wi.parts);
     rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
   } else {
@@ -605,13 +555,6 @@ struct DxCodes {
   uint32_t q2;
   float S;
 };
-
-// dX weight tiles in LDS: row o (0..63) takes 512 bytes; its 16-byte chunk c
-// (columns 8c .. 8c+7) sits at chunk position c ^ wswz(o). With this swizzle
-// the restore stores (16 lanes: 8 rows x 2 blocks, one chunk each) and the
-// transposed fragment reads (32 lanes: 4 rows x 4 chunks, 8 bytes each) both
-// land on 64 distinct banks.
-__device__ __forceinline__ int wswz(int o) { return ((o & 3) << 2) | ((o >> 1) & 3); }
 
 // Restore of one block into a weight tile in 3 + 32 pieces: table, then per
 // code word the four expand pieces, the last of which stores the 8 weights.
@@ -803,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
   if (wi.parts > 1) {
     split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
-                  counters + (wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
+                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
     rlo = 32 * (wi.part * 8 / wi.parts);
     rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
   } else {
@@ -855,7 +798,7 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t nk) {
   const int64_t rounds = tiles / cus, rem = tiles % cus;
   int best = 1;
   int64_t best_cost = rounds * nk + (rem > 0 ? nk : 0);
-  for (int s = 2; s <= kMaxSplit && s <= nk && rem > 0; ++s) {
+  for (int s = 2; s <= kMaxSplit && s <= nk && rem > 0 && rem <= kMaxTileCounters; ++s) {
     const int64_t cost = rounds * nk + (rem * s + cus - 1) / cus * ((nk + s - 1) / s + 24);
     if (cost < best_cost) {
       best_cost = cost;

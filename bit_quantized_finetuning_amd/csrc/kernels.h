@@ -63,6 +63,24 @@ hipError_t launch_gemm_dx(const uint8_t *codes, const uint8_t *qscale, const flo
                           const uint16_t *A, int r, uint16_t *dX, float *partial, uint32_t *counters,
                           hipStream_t st);
 
+// lora_wide.hip: the adapter products for T >= kWideMinTokens.
+constexpr int64_t kWideMinTokens = 65;
+// out[T, r] = P[T, K] . Q[r, K]^T (u = x A^T, v = dY B with Q = B^T); writes
+// out_f32 [T, r] (nullable) and out_bf16 = bf16(scale * out) [T, r_pad]
+// (nullable, zero columns r .. r_pad-1). Uses `partial`
+// (lora_tall_partial_floats) and `counters` (one per 64-token tile).
+hipError_t launch_lora_tall(const uint16_t *P, const uint16_t *Q, int64_t T, int64_t K, int r, int r_pad, float scale,
+                            float *out_f32, uint16_t *out_bf16, float *partial, uint32_t *counters, hipStream_t st);
+size_t lora_tall_partial_floats(int64_t T, int64_t K, int r_pad);
+// X bf16 [T, D], Y float32 [T, R]. y_is_rows: C[R, D] = scale * Y^T X (dA);
+// otherwise C[D, R] = scale * X^T Y (dB). Uses `partial`
+// (lora_wgrad_partial_floats), `counters` (one per output tile) and sets *err
+// if a bounded wait ran out.
+hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64_t D, int64_t R, bool y_is_rows,
+                             float scale, float *C, float *partial, uint32_t *counters, uint32_t *err,
+                             hipStream_t st);
+size_t lora_wgrad_partial_floats(int64_t D, int64_t R, int64_t T);
+
 // lora_grad.hip: C[M, N] = scale * sum_t P[t, m] Q[t, n] over t < T.
 // P and Q are each bf16 or f32 (an f32 operand is split into two bf16 terms).
 hipError_t launch_lora_grad(const void *P, bool P_f32, int64_t M, const void *Q, bool Q_f32, int64_t N,

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = add_dev_u32(&counters[tile], 1u);
+    const uint32_t prev = add_dev_u32(tile_counter(counters, tile), 1u);
     is_last = (prev == (uint32_t)ksplit - 1u);
   }
   __syncthreads();
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const void *__restrict__ Pv, 
       if (m < M && n < N) C[m * N + n] = scale * v[e];
     }
   }
-  if (tid == 0) st_dev_u32(&counters[tile], 0u);
+  if (tid == 0) st_dev_u32(tile_counter(counters, tile), 0u);
 }
 
 int lora_grad_tiles(int64_t M, int64_t N) { return (int)(((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT)); }

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = add_dev_u32(&counters[blockIdx.x], 1u);
+    const uint32_t prev = add_dev_u32(tile_counter(counters, blockIdx.x), 1u);
     is_last = (prev == (uint32_t)ksplit - 1u);
   }
   __syncthreads();
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k_lora_small(const uint16_t *__restrict__
       out_bf16[tt * r_pad + col] = (uint16_t)(pack_bf16x2(sv, 0.f) & 0xffffu);
     }
   }
-  if (tid == 0) st_dev_u32(&counters[blockIdx.x], 0u);
+  if (tid == 0) st_dev_u32(tile_counter(counters, blockIdx.x), 0u);
 }
 
 // 32x32 tiles through LDS.
