@@ -61,14 +61,16 @@ constexpr int kPairsAhead = 2;       // s*u entries per thread read ahead (x kKs
 
 struct GemvCodes {
   u32x4 c0, c1;  // 32 bytes of codes = one 64-weight block
-  uint32_t q2;
+  uint32_t q2;   // its scale code; with kQ4, the aligned word holding the
+                 // codes of blocks 4j..4j+3 of the row (the byte is picked
+                 // when used, so no loaded value is reshaped while in flight)
   float S;
 };
 struct GemvX {
   u32x4 x[8];  // 64 bf16 of one token row (global-x path only)
 };
 
-template <int kW, bool kXL>
+template <int kW, bool kXL, bool kQ4>
 __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ qscale, const float *__restrict__ smax,
     int d_out, int d_in, const uint16_t *__restrict__ x, int T, const uint16_t *__restrict__ A,
@@ -114,7 +116,9 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     const uint32_t blk = (uint32_t)row * (uint32_t)KB + (uint32_t)kb;
     st.c0 = bld16(cr, ok ? blk * 32u : kOOB);
     st.c1 = bld16(cr, ok ? blk * 32u + 16u : kOOB);
-    st.q2 = bld8(qr, ok ? blk : kOOB);
+    // kQ4 (blocks per row a multiple of 4): the word of blocks kb - g .. kb - g + 3
+    // lies in the row, so inside the tensor
+    st.q2 = kQ4 ? bld32(qr, ok ? (blk & ~3u) : kOOB) : bld8(qr, ok ? blk : kOOB);
     st.S = __uint_as_float(bld32(sr, ok ? (blk >> 8) * 4u : kOOB));
   };
   auto load_x = [&](int s, GemvX &st) {
@@ -184,11 +188,32 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   if (producer) a_issue(0);
   if (kXL && mseg > 0) x_issue(0);
 
-  GemvCodes ca, cb;
-  GemvX xa, xb;
+  // Items (row tile k, segment s) in order k * mseg + s, through a ring of
+  // kStages register stages: kStages - 1 items are in flight while one is
+  // computed. Two stages measure fastest: the restore (about 270 VALU
+  // instructions per wave and item) and the fixed launch and first-load
+  // latency bound this kernel, not the bytes in flight, and deeper rings
+  // (3 or 4 stages, measured) only delay the first data. Items past the last
+  // row tile read rows >= d_out, which load as zeros without touching memory.
+  constexpr int kStages = 2;
+  GemvCodes cq[kStages];
+  GemvX xg[kXL ? 1 : kStages];
+  auto advance = [&](int &k, int &s) {
+    if (++s == mseg) {
+      s = 0;
+      ++k;
+    }
+  };
+  int kl = 0, sl = 0;  // next item to load
   if (mseg > 0) {
-    load_codes(0, 0, ca);
-    if (!kXL) load_x(0, xa);
+#pragma unroll
+    for (int j = 0; j + 1 < kStages; ++j) {
+      load_codes(kl, sl, cq[j]);
+      if (!kXL) load_x(sl, xg[j]);
+      advance(kl, sl);
+      // the stages go out in ring order (the waits count on it)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   u32x4 bpre[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   const rsrc_t br = make_rsrc(B, (int64_t)d_out * r * 2);
@@ -250,9 +275,11 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   // ---------------- s*u exchange: read ahead, check at the first row-tile end ----------------
   // Thread tid owns entries (t, col) = tid + i kThreads of the T x r_pad
   // intermediate and reads their kKsp partials; the first kPairsAhead go out
-  // before the last item of the first row tile.
+  // before the last item of the first row tile. (A second round kept in
+  // flight measured slower: every round reads all kKsp tagged partials, which
+  // competes with the weight stream.)
   const int npair = T * r_pad;
-  uint64_t pv[kPairsAhead][kKsp];
+  uint64_t pv0[kPairsAhead][kKsp];
   auto poll_load = [&](int i, uint64_t (&dst)[kKsp]) {
     const int p = tid + i * kThreads;
     const int t = p / r_pad, col = p - t * r_pad;
@@ -261,7 +288,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       dst[ks] = p < npair ? ld_dev_u64(uex + (ks * 16 + t) * r_pad + col) : ((uint64_t)tag << 32);
   };
   bool polled = false;
-  auto poll_issue = [&]() {
+  auto poll_issue = [&](uint64_t (&pv)[kPairsAhead][kKsp]) {
 #pragma unroll
     for (int i = 0; i < kPairsAhead; ++i) poll_load(i, pv[i]);
     polled = true;
@@ -269,7 +296,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int s, const GemvCodes &cs, const GemvX &xs2) {
-    const Nf4Planes t = make_planes(restore_scale(cs.q2, cs.S));
+    const Nf4Planes t = make_planes(restore_scale(kQ4 ? (cs.q2 >> (8 * g)) & 0xffu : cs.q2, cs.S));
     // LDS path: token rows >= T only feed accumulator rows that are never stored,
     // and a block past the row end has an all-zero restore table, so both read
     // clamped, staged x without masking
@@ -292,8 +319,11 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       // the kKsp partials in slice order (the same on every workgroup);
       // workgroup 0 also writes float32 u. Rows t >= T of su_l only feed
       // accumulator rows that are never stored.
-      if (!polled) poll_issue();
-      for (int it = 0;; ++it) {
+      // One round: write every entry whose partials all carry this launch's
+      // tag; returns whether any entry of the workgroup was not ready (two
+      // flag rows in turn: a row is rewritten only two barriers after it was
+      // last read).
+      auto check = [&](const uint64_t (&pv)[kPairsAhead][kKsp], int it) {
         int bad = 0;
         for (int i = 0; i * kThreads < npair; ++i) {
           uint64_t e[kKsp];
@@ -319,21 +349,23 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
             if (u_out && cid == 0 && col < r) u_out[t * r + col] = u;
           }
         }
-        // workgroup OR of `bad` (two flag rows in turn: a row is rewritten only
-        // two barriers after it was last read)
         const int wbad = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0ull ? 1 : 0);
         if (lane == 0) poll_bad[it & 1][wave] = wbad;
         lds_barrier();
         int any = 0;
 #pragma unroll
         for (int w = 0; w < kW; ++w) any |= poll_bad[it & 1][w];
-        if (!any) break;
+        return any != 0;
+      };
+      if (!polled) poll_issue(pv0);
+      for (int it = 0;; ++it) {
+        if (!check(pv0, it)) break;
         if (it >= kSpinLimit) {
           if (tid == 0) st_dev_u32(&sync[3], 1u);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
-        poll_issue();
+        poll_issue(pv0);
       }
     }
     if (P > 0 && wave == 0) {
@@ -370,28 +402,28 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   if (mseg == 0) {
     for (int k = 0; k < nrt; ++k) epilogue(k);
   } else {
-    // Two stages in ping-pong: compute one item while the next one's loads fly.
-    int k = 0, s = 0;
-    while (true) {
-      int k2 = k, s2 = s + 1;
-      if (s2 == mseg) { s2 = 0; ++k2; }
-      load_codes(k2, s2, cb);
-      if (!kXL) load_x(s2, xb);
-      if (P > 0 && k == 0 && s == mseg - 1) poll_issue();
-      compute(s, ca, xa);
-      if (s == mseg - 1) epilogue(k);
-      k = k2, s = s2;
-      if (k >= nrt) break;
-
-      k2 = k, s2 = s + 1;
-      if (s2 == mseg) { s2 = 0; ++k2; }
-      load_codes(k2, s2, ca);
-      if (!kXL) load_x(s2, xa);
-      if (P > 0 && k == 0 && s == mseg - 1) poll_issue();
-      compute(s, cb, xb);
-      if (s == mseg - 1) epilogue(k);
-      k = k2, s = s2;
-      if (k >= nrt) break;
+    // The ring, unrolled kStages times so that every stage has fixed registers:
+    // step u refills the stage freed by step u - 1, then computes stage u.
+    // The loop has one exit, after a whole turn of the ring (the item count is
+    // rounded up; items past the last row tile compute on zeros and skip the
+    // epilogue), and the steps keep their order: then each stage's wait
+    // covers only its own loads. (An exit inside the turn, or loads moved
+    // across steps, makes the compiler wait for every stage at once.)
+    const int nitems = nrt * mseg;
+    int k = 0, s = 0;  // item being computed
+    for (int i = 0; i < nitems; i += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        load_codes(kl, sl, cq[(u + kStages - 1) % kStages]);
+        if (!kXL) load_x(sl, xg[(u + kStages - 1) % kStages]);
+        advance(kl, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (P > 0 && k == 0 && s == mseg - 1) poll_issue(pv0);
+        compute(s, cq[u], xg[kXL ? 0 : u]);
+        if (s == mseg - 1 && k < nrt) epilogue(k);
+        advance(k, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -435,17 +467,27 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
   if (G < P) G = P;
   const size_t xbytes = (size_t)T * (d_in + kXPad) * 2;
   const int di = (int)d_in, dn = (int)d_out, Tt = (int)T;
+  const bool q4 = (d_in / kBlock) % 4 == 0;
   if (xbytes <= (size_t)kXLdsBytes) {
     if (dev >= 0 && !g_gemv_attr[dev]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsBytes);
-      if (e != hipSuccess) return e;
+      for (const void *f : {reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, true>),
+                            reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, false>)}) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsBytes);
+        if (e != hipSuccess) return e;
+      }
       g_gemv_attr[dev] = true;
     }
-    k_gemv_fwd<kGvW, true><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
+    if (q4)
+      k_gemv_fwd<kGvW, true, true><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
+          codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+    else
+      k_gemv_fwd<kGvW, true, false><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
+          codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+  } else if (q4) {
+    k_gemv_fwd<kGvW, false, true><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
         codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
   } else {
-    k_gemv_fwd<kGvW, false><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
+    k_gemv_fwd<kGvW, false, false><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
         codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
   }
   return hipGetLastError();
