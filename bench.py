@@ -22,8 +22,14 @@ group maxima per second); `roofline` is the weight-streaming kernel's algorithmi
 bytes per launch over its mean launch duration in the timed region; `cpu_baseline`
 is the CPU oracle timed on a bounded sample of the same workload.
 
-Other workloads (--workload 13b_4096tok / 65b_layer / linear1024) time the MFMA
-GEMM regime (forward + backward); they are records, not the headline line.
+Other workloads are records, not the headline line:
+  13b_4096tok / 65b_layer / linear1024 / 14b_stack  the MFMA GEMM regime
+      (forward + backward; 14b_stack: one of the 40 identical layers of the
+      14B-style stack, bf16 source weights, 2048 tokens, LoRA r=8 on q and v);
+  14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack
+      (13.2 G parameters, generated on the device from a seeded generator);
+  merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two
+      LLaMA-7B projections with r = 64.
 """
 
 from __future__ import annotations
@@ -42,7 +48,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer"]
+WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_quantize",
+                    "merge_llama7b"]
 
 
 def parse():
@@ -101,6 +108,10 @@ def main():
     from bit_quantized_finetuning_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.workload == "merge_llama7b":
+        return bench_merge(args, torch, q, synth, dev)
+    if args.workload == "14b_quantize":
+        return bench_quantize_stack(args, torch, q, synth, dev)
     wl = synth.WORKLOADS[args.workload]
     seed_cfg = synth.WORKLOAD_SEED[args.workload]
     bw = bool(wl.backward)
@@ -256,7 +267,8 @@ def main():
         "config": {"workload": wl.description, "projections": [f"{p.d_out}x{p.d_in}" for p in wl.projections],
                    "tokens": list(wl.tokens), "lora_r": wl.projections[0].r, "lora_alpha": wl.projections[0].alpha,
                    "backward": bw, "graph_steps": chunk if graphs else 0,
-                   "weight_copies_per_projection": len(projs[0][1])},
+                   "weight_copies_per_projection": len(projs[0][1]),
+                   **({"layers_in_stack": wl.layers, "layers_per_step": 1} if wl.layers > 1 else {})},
         "tflops": round(tflops, 3),
         "total_GBs": round((fb + bb) / (ms_step * 1e-3) / 1e9, 1),
         "roofline": roof,
@@ -352,6 +364,168 @@ def cpu_baseline(args, wl, seed_cfg, wbytes_step):
             "sample": f"{done_steps} full step(s) of the same workload (restore + float64 forward of every "
                       f"projection and token count; quantization untimed), {el:.1f} s",
             "ms_per_step": round(sec_step * 1e3, 1)}
+
+
+def _timed_graph(torch, dev, body, steps, chunk):
+    """Capture `body(k)` for k in 0..chunk-1 into a graph; return ms per step over `steps` steps
+    (HIP events on the replay stream, a whole number of replays)."""
+    side = torch.cuda.Stream(dev)  # default priority
+    for k in range(chunk):
+        body(k)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for k in range(chunk):
+            body(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    reps = max(1, (steps + chunk - 1) // chunk)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * chunk), reps * chunk
+
+
+def _line(args, value, unit, ms_step, steps, workload, roof, cpu, extra=None, higher=True):
+    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5), "higher_is_better": higher, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded N(0,0.02^2) weights and adapters)",
+            "config": {"workload": workload}, "roofline": roof, "cpu_baseline": cpu}
+    line.update(extra or {})
+    print(json.dumps(line), flush=True)
+
+
+def merge_bytes(d_out, d_in, r):
+    """Algorithmic HBM bytes of one merge: NF4 weight + A, B in; bf16 merged weight out."""
+    return weight_bytes(d_out, d_in) + 2 * r * (d_in + d_out) + 2 * d_out * d_in
+
+
+def bench_merge(args, torch, q, synth, dev):
+    """Merge for export of the two LLaMA-7B projections (r = 64): one step = both merges, each one launch of
+    k_merge; every launch of a graph reads its own weight copy and writes its own output."""
+    wl = synth.WORKLOADS["llama7b_skinny"]
+    cfg = synth.WORKLOAD_SEED["llama7b_skinny"]
+    chunk = min(args.chunk, 10)
+    items = []
+    for pi, p in enumerate(wl.projections):
+        W = torch.from_numpy(synth.weight(cfg, pi, p.d_out, p.d_in)).to(dev)
+        w0 = q.qlora_quantize(W)
+        del W
+        (_, A_bits), (_, B_bits) = synth.adapters(cfg, pi, p.d_out, p.d_in, p.r)
+        A = torch.from_numpy(np.ascontiguousarray(A_bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        B = torch.from_numpy(np.ascontiguousarray(B_bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        ws = [(q.NF4Weight(p.d_out, p.d_in, w0.codes.clone(), w0.qscale.clone(), w0.smax.clone()),
+               torch.empty(p.d_out, p.d_in, dtype=torch.bfloat16, device=dev)) for _ in range(chunk)]
+        items.append((p, A, B, ws))
+    for _ in range(max(args.warmup, 1)):
+        for p, A, B, ws in items:
+            q.qlora_merge(ws[0][0], A, B, p.alpha, out=ws[0][1])
+
+    def body(k):
+        for p, A, B, ws in items:
+            wc, out = ws[k]
+            q.qlora_merge(wc, A, B, p.alpha, out=out)
+
+    ms_step, steps = _timed_graph(torch, dev, body, args.steps, chunk)
+    nbytes = sum(merge_bytes(p.d_out, p.d_in, p.r) for p, *_ in items)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    us_launch = ms_step * 1e3 / len(items)
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_merge (qlora_merge)",
+            "bytes_per_launch": round(nbytes / len(items)), "us_per_launch": round(us_launch, 3),
+            "launches": steps * len(items)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count()
+        rows, prepared = 256, []
+        for pi, p in enumerate(wl.projections):
+            W = synth.weight(cfg, pi, rows, p.d_in)  # a 256-row weight of the same distribution
+            codes, q2, S = oracle.quantize(W)
+            (A, _), (B, _) = synth.adapters(cfg, pi, p.d_out, p.d_in, p.r)
+            prepared.append((p, codes, q2, S, A, B[:rows]))
+        done, t_start = 0, time.perf_counter()
+        while True:
+            for p, codes, q2, S, A, Bs in prepared:
+                _, wb = oracle.dequantize(codes, q2, S, rows, p.d_in)
+                oracle.lora_merge(wb, A, Bs, p.alpha, p.r)
+            done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds:
+                break
+        sb = sum(merge_bytes(rows, p.d_in, p.r) for p, *_ in prepared)
+        cpu = {"value": round(sb * done / el / 1e9, 4), "unit": "GB/s (merge algorithmic bytes per second)",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{done} pass(es) over {rows}-row slices of both projections (restore + float64 merge), "
+                         f"{el:.1f} s"}
+    _line(args, round(gbs, 1), "GB/s (merge algorithmic bytes per second)", ms_step, steps,
+          "merge for export, bf16(W_hat + (alpha/r) B A), LLaMA-7B projections 4096x4096 and 11008x4096, "
+          "LoRA r=64 alpha=16", roof, cpu,
+          {"per_launch_us": round(us_launch, 3), "graph_steps": chunk})
+
+
+def bench_quantize_stack(args, torch, q, synth, dev):
+    """One pass quantizing all 280 bf16 weights of the 14B-style stack (40 layers x q, k, v, o, gate, up, down):
+    one step = the whole pass, 280 launches of k_quantize. Weights come from a seeded device generator
+    (N(0, 0.02^2) rounded to bf16); 13.2 G weights are too many to draw on the host."""
+    wl = synth.WORKLOADS["14b_stack"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.WORKLOAD_SEED["14b_stack"])
+    Ws, outs = [], []
+    for layer in range(wl.layers):
+        for p in wl.projections:
+            W = torch.empty(p.d_out, p.d_in, dtype=torch.bfloat16, device=dev)
+            W.normal_(0.0, 0.02, generator=gen)
+            Ws.append(W)
+            outs.append(q.NF4Weight.empty(p.d_out, p.d_in, dev))
+    torch.cuda.synchronize()
+
+    def body(k):
+        for W, o in zip(Ws, outs):
+            q.qlora_quantize(W, out=o)
+
+    ms_step, steps = _timed_graph(torch, dev, body, args.steps, 1)
+    n = sum(W.numel() for W in Ws)
+    nbytes = sum(2 * W.numel() + q.qlora_storage_bytes(W.shape[0], W.shape[1]) for W in Ws)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_quantize<bf16> (qlora_quantize)",
+            "bytes_per_launch": round(nbytes / len(Ws)), "us_per_launch": round(ms_step * 1e3 / len(Ws), 3),
+            "launches": steps * len(Ws)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count()
+        Wh = synth.weight(synth.WORKLOAD_SEED["14b_stack"], 0, 256, 5120, "bf16")
+        done, t_start = 0, time.perf_counter()
+        while True:
+            oracle.quantize(Wh)
+            done += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds:
+                break
+        sb = (2 * Wh.size + q.qlora_storage_bytes(256, 5120)) * done
+        cpu = {"value": round(sb / el / 1e9, 4), "unit": "GB/s (quantize algorithmic bytes per second)",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{done} quantization(s) of a 256x5120 bf16 slice, {el:.1f} s"}
+    _line(args, round(gbs, 1), "GB/s (quantize algorithmic bytes per second: bf16 in, NF4 + double quant out)",
+          ms_step, steps, f"one-pass quantize of the 14B-style stack: {len(Ws)} bf16 weights, {n / 1e9:.2f} G "
+          "parameters", roof, cpu, {"weights": len(Ws), "params": n, "ms_per_pass": round(ms_step, 3)})
 
 
 if __name__ == "__main__":

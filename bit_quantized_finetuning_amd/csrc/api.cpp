@@ -216,6 +216,20 @@ int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStr
                                       consts(), stream));
 }
 
+int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                uint16_t *out, hipStream_t stream) {
+  int s = validate_weight(W);
+  if (s) return s;
+  if (!out) return QLORA_ERR_NULL;
+  if (r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (!A && !B) r = 0;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(out) || (r > 0 && (!aligned16(A) || !aligned16(B)))) return QLORA_ERR_ALIGN;
+  const float sc = r > 0 ? alpha / (float)r : 0.f;
+  return hip_status(launch_merge(W->codes, W->qscale, W->smax, W->d_out, W->d_in, r > 0 ? A : nullptr,
+                                 r > 0 ? B : nullptr, r, sc, out, stream));
+}
+
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
                   int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, size_t ws_bytes,
                   hipStream_t stream) {

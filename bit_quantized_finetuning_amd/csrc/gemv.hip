@@ -82,7 +82,6 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
                "s"(A), "s"(B), "s"(r), "s"(r_pad), "s"(scale), "s"(h), "s"(u_out), "s"(uex), "s"(sync),
                "s"(gridDim.x));
   constexpr int kThreads = 64 * kW;
-  constexpr int kPollPer = 16 * kMaxRpad / 2 / kThreads;  // tagged pairs per thread, at most
   extern __shared__ __attribute__((aligned(16))) uint16_t x_l[];  // [T][d_in + kXPad] when kXL
   __shared__ float red[kW][256];
   __shared__ __attribute__((aligned(16))) uint16_t su_l[16 * kMaxRpad];

@@ -16,6 +16,8 @@ hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const float *smax,
                              int64_t d_out, int64_t d_in, bool bf16_out, void *out, const Nf4Consts &c,
                              hipStream_t st);
+hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out, int64_t d_in,
+                        const uint16_t *A, const uint16_t *B, int r, float scale, uint16_t *out, hipStream_t st);
 
 // lora_small.hip: out[T, r] = P[T, K] . Q^T with Q given as [r, K] (K contiguous).
 // Writes out_f32 (nullable) and out_bf16 = bf16(scale * out) with row pitch r_pad

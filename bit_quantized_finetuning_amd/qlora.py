@@ -6,7 +6,7 @@ allocates nothing. If the library is missing this module raises at import --
 there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
-    qlora_quantize, qlora_dequantize, qlora_forward, qlora_backward,
+    qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_backward,
     qlora_storage_bytes, qlora_workspace_bytes, qlora_nf4_codebook,
     qlora_nf4_thresholds, qlora_status_string
 """
@@ -50,6 +50,8 @@ _lib.qlora_quantize.argtypes = [_vp, ctypes.c_int, _W, _vp, _vp]
 _lib.qlora_quantize.restype = ctypes.c_int
 _lib.qlora_dequantize.argtypes = [_W, ctypes.c_int, _vp, _vp]
 _lib.qlora_dequantize.restype = ctypes.c_int
+_lib.qlora_merge.argtypes = [_W, _vp, _vp, _i32, _f32, _vp, _vp]
+_lib.qlora_merge.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
 _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -192,6 +194,20 @@ def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:
     dt = BF16 if dtype == torch.bfloat16 else F32
     cw = w._c()
     _check(_lib.qlora_dequantize(ctypes.byref(cw), dt, _ptr(out), _stream(out.device)), "qlora_dequantize")
+    return out
+
+
+def qlora_merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [d_out, d_in] = bf16(W_hat + (alpha/r) B A): the adapter merged into the restored weight."""
+    r = 0 if A is None else A.shape[0]
+    if A is not None:
+        _bits(A), _bits(B)
+    if out is None:
+        out = torch.empty(w.d_out, w.d_in, dtype=torch.bfloat16, device=w.codes.device)
+    cw = w._c()
+    _check(_lib.qlora_merge(ctypes.byref(cw), _ptr(A), _ptr(B), r, alpha, _ptr(out), _stream(out.device)),
+           "qlora_merge")
     return out
 
 

@@ -103,6 +103,23 @@ int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint
 int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStream_t stream);
 
 /*
+ * Merge a trained adapter into the restored weight, for export ("48GB GPU
+ * Fine-Tuning a 65B Model: Where QLoRA Saves GPU Memory", section "QLoRA Puts
+ * the Two Methods in Different Places": A and B cannot be added to the 4-bit
+ * weights and are merged into the restored 16-bit weights).
+ *   A    device bf16 [r, d_in], B device bf16 [d_out, r]; r = 0 or A = B = NULL
+ *        gives the plain bf16 restore
+ *   out  device bf16 [d_out, d_in], written in full; 16-byte aligned
+ * out = bf16( w_hat + fl32(s * (B A)) ) with s = alpha / r in float32, B A
+ * accumulated in float32 and one round-to-nearest-even at the end: within one
+ * bf16 unit in the last place of the exactly rounded merge. The weight buffers
+ * are only read. Errors: NULL, SHAPE (r outside 0..256 or r % 8 != 0), ALIGN,
+ * HIP (launch failure); nothing is written on a validation error.
+ */
+int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                uint16_t *out, hipStream_t stream);
+
+/*
  * Forward h = x W_hat^T + (alpha/r) (x A^T) B^T ("QLoRA의 수식").
  *   x      device bf16 [T, d_in]
  *   A, B   device bf16 [r, d_in], [d_out, r]; both NULL, or r == 0, means base only

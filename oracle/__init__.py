@@ -39,4 +39,4 @@ from .nf4 import (  # noqa: F401
     dequantize,
     storage_bytes,
 )
-from .qlora import lora_forward, lora_backward  # noqa: F401
+from .qlora import lora_forward, lora_backward, lora_merge, bf16_round_f64  # noqa: F401

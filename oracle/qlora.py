@@ -22,6 +22,12 @@ B). For an upstream gradient dY = dL/dh [T, d_out]:
     dB = (alpha/r) dY^T u             [d_out, r]
 No dW is produced.
 
+Merge ([48GB] "QLoRA Puts the Two Methods in Different Places": the trained A
+and B cannot be added to the 4-bit weights; they are merged into the restored
+16-bit weights):
+    W_merged = bf16(W_hat + (alpha/r) B A)
+with the sum exact in float64 and a single round-to-nearest-even to bf16.
+
 All products are float64 matrix products of the given (bf16-exact) values;
 the result is the exact value up to float64 rounding.
 """
@@ -69,3 +75,27 @@ def lora_backward(W_hat: np.ndarray, x: np.ndarray, dY: np.ndarray, A: np.ndarra
     dA = s * (v.T @ xd)
     dB = s * (gd.T @ u)
     return dX, dA, dB
+
+
+def bf16_round_f64(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 in one step (nearest, ties to even), as float64.
+
+    Finite values in the bf16 range only. A bf16 keeps 8 significant bits: with
+    a = m 2^e, 0.5 <= |m| < 1, the result is rint(m 2^8) 2^(e-8) (numpy's rint
+    rounds halves to even). Below the smallest normal (2^-126) the spacing is
+    fixed at 2^-133.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    normal = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    sub = np.ldexp(np.rint(np.ldexp(a, 133)), -133)
+    return np.where(np.abs(a) < 2.0 ** -126, sub, normal)
+
+
+def lora_merge(W_hat: np.ndarray, A: np.ndarray | None, B: np.ndarray | None, alpha: float, r: int) -> np.ndarray:
+    """bf16(W_hat + (alpha/r) B A) as float64 values; r == 0 (or A/B None) returns W_hat rounded (unchanged)."""
+    Wd = np.asarray(W_hat, dtype=np.float64)
+    if r == 0 or A is None or B is None:
+        return bf16_round_f64(Wd + 0.0)
+    exact = Wd + _scale(alpha, r) * (np.asarray(B, dtype=np.float64) @ np.asarray(A, dtype=np.float64))
+    return bf16_round_f64(exact)

@@ -45,6 +45,34 @@ def assert_close(name, gpu, ref):
     assert mx <= MAX_ABS, f"{name}: max-abs error {mx:.3e} > {MAX_ABS} * max|ref|"
 
 
+def merge_float32_slack(wb, A, B, alpha, r):
+    """Bound on the float32 error of forming W_hat + s B A before the final bf16 rounding: the products
+    are exact, r accumulations and the scale and add roundings each cost at most 2^-24 of the operands'
+    magnitudes. Where W_hat and s B A nearly cancel this exceeds an ulp of the small result."""
+    if r == 0 or A is None:
+        return 0.0
+    s = float(np.float32(alpha) / np.float32(r))
+    return 2.0 ** -24 * (np.abs(wb) + (r + 2) * s * (np.abs(np.asarray(B, np.float64)) @ np.abs(np.asarray(A, np.float64))))
+
+
+def assert_within_one_bf16_ulp(name, gpu, ref, slack=0.0, max_mismatch=1e-3):
+    """gpu: bf16 tensor; ref: float64 values already rounded to bf16 (the oracle's single rounding).
+    Every element within one bf16 unit in the last place of the larger magnitude plus `slack` (the
+    float32 error of the library's sum, see merge_float32_slack), and at most max_mismatch of them
+    off at all."""
+    g = gpu.detach().float().cpu().numpy().astype(np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape
+    mag = np.maximum(np.abs(g), np.abs(r))
+    ulp = np.where(mag > 0, np.ldexp(1.0, np.frexp(mag)[1] - 8), 0.0)
+    diff = np.abs(g - r)
+    frac = float(np.mean(diff > 0))
+    say(f"    {name}: max diff/ulp={np.max(np.where(ulp > 0, diff / np.where(ulp > 0, ulp, 1), 0)):.2f} "
+        f"max diff/(ulp+slack)={np.max(diff / np.maximum(ulp + slack, 1e-300)):.2f} mismatch fraction={frac:.2e}")
+    assert np.all(diff <= ulp + slack), f"{name}: an element is off by more than one bf16 ulp + float32 slack"
+    assert frac <= max_mismatch, f"{name}: {frac:.2e} of the elements differ"
+
+
 class Case:
     """Seeded inputs for one projection plus lazily computed oracle quantities."""
 

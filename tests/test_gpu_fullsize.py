@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from bit_quantized_finetuning_amd import synth
-from gpu_common import assert_close, bits_to_bf16, say
+from gpu_common import assert_close, assert_within_one_bf16_ulp, bits_to_bf16, merge_float32_slack, say
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +139,19 @@ def test_single_linear_seed0_full():
     for name, g, ref in [("h", h, h_ref), ("u", u, u_ref), ("dX", dX, dX_ref), ("dA", dA, dA_ref),
                          ("dB", dB, dB_ref)]:
         assert_close(name, g, ref)
+
+
+def test_merge_llama7b_full():
+    """Merge for export of a LLaMA-7B projection (4096 x 4096, r = 64), the configuration the benchmark
+    times: every element within one bf16 ulp (plus the float32 summation bound where W_hat and s B A
+    nearly cancel) of the exactly rounded merge (48GB page, "QLoRA Puts the Two Methods in Different
+    Places")."""
+    cfg, r, alpha, d = synth.WORKLOAD_SEED["llama7b_skinny"], 64, 16.0, 4096
+    say("full merge 4096x4096 r=64")
+    W_np = synth.weight(cfg, 0, d, d)
+    w, wb = _quantize_full(W_np)
+    (A, A_bits), (B, B_bits) = synth.adapters(cfg, 0, d, d, r)
+    out = q.qlora_merge(w, bits_to_bf16(A_bits), bits_to_bf16(B_bits), alpha)
+    torch.cuda.synchronize()
+    assert_within_one_bf16_ulp("merged", out, oracle.lora_merge(wb, A, B, alpha, r),
+                               merge_float32_slack(wb, A, B, alpha, r))

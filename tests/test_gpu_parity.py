@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import Case, assert_close, bits_to_bf16, say
+from gpu_common import Case, assert_close, assert_within_one_bf16_ulp, bits_to_bf16, merge_float32_slack, say
 
 pytestmark = pytest.mark.gpu
 
@@ -248,3 +248,51 @@ def test_skinny_forward_call_sequence():
         assert_close("h", h, h_ref)
         assert_close("u", u, u_ref)
     _assert_workspace_clean()
+
+
+# ---------------------------------------------------------------------------
+# LoRA-FA (A frozen): the backward without dA needs no layer input
+# (GPU-fit page, "LoRA 변형을 바꿔도 답이 같은 이유": LoRA-FA keeps no layer input)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_lora_fa_backward_needs_no_input(T):
+    say(f"LoRA-FA backward T={T}")
+    case = Case(272, 320, 64, T, cfg=117)
+    w, d = _quantize_and_compare(case)
+    _, u = q.qlora_forward(w, d["x"], d["A"], d["B"], case.alpha, save_u=True)
+    dX, dA, dB = q.qlora_backward(w, None, d["dY"], d["A"], d["B"], case.alpha, u_saved=u, need_dA=False)
+    torch.cuda.synchronize()
+    assert dA is None
+    dX_ref, _, dB_ref = case.oracle_backward()
+    assert_close("dX", dX, dX_ref)
+    assert_close("dB", dB, dB_ref)
+
+
+# ---------------------------------------------------------------------------
+# merge for export (48GB page, "QLoRA Puts the Two Methods in Different Places")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,r", [(1024, 1024, 8), (80, 320, 16), (272, 5120, 64), (528, 1344, 256),
+                                          (16, 64, 8)])
+def test_merge_parity(d_out, d_in, r):
+    say(f"merge {d_out}x{d_in} r={r}")
+    case = Case(d_out, d_in, r, 1, cfg=118)
+    w, d = _quantize_and_compare(case)
+    out = q.qlora_merge(w, d["A"], d["B"], case.alpha)
+    torch.cuda.synchronize()
+    wb = case.oracle_quant()[4]
+    assert_within_one_bf16_ulp("merged", out, oracle.lora_merge(wb, case.A, case.B, case.alpha, r),
+                               merge_float32_slack(wb, case.A, case.B, case.alpha, r))
+
+
+def test_merge_without_adapter_is_the_restore():
+    say("merge r=0 / B=0")
+    case = Case(80, 320, 16, 1, cfg=119)
+    w, d = _quantize_and_compare(case)
+    wb = case.oracle_quant()[4]
+    plain = q.qlora_merge(w, None, None, case.alpha)
+    zero_b = q.qlora_merge(w, d["A"], torch.zeros_like(d["B"]), case.alpha)
+    torch.cuda.synchronize()
+    for t in (plain, zero_b):
+        assert np.array_equal(t.float().cpu().numpy(), wb)  # values; a -0.0 restore comes back +0.0

@@ -152,3 +152,54 @@ def test_lora_parameter_counts_from_pages():
             n += p.r * (p.d_in + p.d_out)
     n *= wl.layers
     assert round(n / 1e6, 2) == g["qwen3_14b_lora_q_v_r8_params"]["value"] / 1e6
+
+
+# ---------------------------------------------------------------------------
+# merge (48GB, "QLoRA Puts the Two Methods in Different Places": A and B are
+# merged into the restored 16-bit weights)
+# ---------------------------------------------------------------------------
+
+def test_merge_columns_are_forward_of_unit_tokens():
+    """Column k of the merged weight is the forward of the k-th unit token, rounded once to bf16:
+    pins the orientation (B A, not A^T B^T) and the scale against the forward oracle."""
+    Wh, _, A, B, _ = _setup(24, 64, 8, 1, seed=5)
+    merged = oracle.lora_merge(Wh, A, B, 16.0, 8)
+    h, _ = oracle.lora_forward(Wh, np.eye(64), A, B, 16.0, 8)  # h[k, n] = W_merged_exact[n, k]
+    assert np.array_equal(merged, oracle.bf16_round_f64(h.T))
+
+
+def test_merge_zero_B_is_the_restored_weight():
+    Wh, _, A, B, _ = _setup(24, 64, 8, 1, seed=6)
+    merged = oracle.lora_merge(Wh, A, np.zeros_like(B), 16.0, 8)
+    assert np.array_equal(merged, Wh.astype(np.float64))  # values (a -0.0 restore may come back +0.0)
+    assert np.array_equal(oracle.lora_merge(Wh, None, None, 16.0, 0), Wh.astype(np.float64))
+
+
+def test_merge_rounds_once_to_nearest_even():
+    """Constructed ties: with s = 1 (alpha = r = 8) and s B A = k 2^-8 added to 1.0, whose bf16
+    spacing is 2^-7: k = 1 is a tie between 1 and 1 + 2^-7 (even: 1), k = 3 a tie between
+    1 + 2^-7 and 1 + 2^-6 (even: 1 + 2^-6); a hair above a tie rounds up."""
+    r = 8
+    Wh = np.ones((3, 64), dtype=np.float32)
+    A = np.zeros((r, 64), dtype=np.float32)
+    B = np.zeros((3, r), dtype=np.float32)
+    A[0, :] = 2.0 ** -4
+    B[0, 0], B[1, 0], B[2, 0] = 2.0 ** -4, 3 * 2.0 ** -4, 2.0 ** -4
+    A[1, 5] = 2.0 ** -20
+    B[2, 1] = 1.0  # row 2, column 5: 1 + 2^-8 + 2^-20
+    m = oracle.lora_merge(Wh, A, B, 8.0, r)
+    assert np.all(m[0] == 1.0)
+    assert np.all(m[1] == 1.0 + 2.0 ** -6)
+    assert m[2, 5] == 1.0 + 2.0 ** -7 and m[2, 4] == 1.0
+
+
+def test_bf16_round_f64_agrees_with_float32_route_on_float32_values():
+    """For values already in float32 the one-step float64 rounding and the float32 bit rounding
+    (written independently) must agree bit for bit, including every tie."""
+    rs = np.random.default_rng(7)
+    v = rs.standard_normal(20000).astype(np.float32) * np.float32(0.03)
+    ties = (np.arange(1, 2001, dtype=np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)  # subnormal
+    nties = ((np.arange(0x3C00, 0x3C00 + 2000, dtype=np.uint32) << 16) | np.uint32(0x8000)).view(np.float32)
+    for a in (v, ties, -ties, nties, -nties):
+        ref = oracle.bf16_round(a).astype(np.float64)
+        assert np.array_equal(oracle.bf16_round_f64(a.astype(np.float64)), ref)
