@@ -799,7 +799,14 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t nk) {
   int best = 1;
   int64_t best_cost = rounds * nk + (rem > 0 ? nk : 0);
   for (int s = 2; s <= kMaxSplit && s <= nk && rem > 0 && rem <= kMaxTileCounters; ++s) {
-    const int64_t cost = rounds * nk + (rem * s + cus - 1) / cus * ((nk + s - 1) / s + 24);
+    // Cost in K steps of one tile. When the split tail shares rounds with other
+    // work, each round pays for moving its partials through memory (24 steps
+    // measured at the 13B/65B shapes). When the whole launch is one round of
+    // split tiles, the combine is one tile's store and re-read per part, about
+    // three steps.
+    const int64_t cost = (rounds == 0 && rem * s <= cus)
+                             ? (nk + s - 1) / s + 3
+                             : rounds * nk + (rem * s + cus - 1) / cus * ((nk + s - 1) / s + 24);
     if (cost < best_cost) {
       best_cost = cost;
       best = s;
