@@ -16,13 +16,15 @@ hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const float *smax,
                              int64_t d_out, int64_t d_in, bool bf16_out, void *out, const Nf4Consts &c,
                              hipStream_t st);
+
+// merge.hip: out[d_out, d_in] = bf16(W_hat + scale B A), A [r, d_in], B [d_out, r] bf16 (r may be 0).
 hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out, int64_t d_in,
                         const uint16_t *A, const uint16_t *B, int r, float scale, uint16_t *out, hipStream_t st);
 
 // lora_small.hip: out[T, r] = P[T, K] . Q^T with Q given as [r, K] (K contiguous).
 // Writes out_f32 (nullable) and out_bf16 = bf16(scale * out) with row pitch r_pad
 // (zero-filled up to r_pad, a multiple of 16). Uses `partial` (ksplit*16*r_pad f32
-// per 16-token tile) and `counters` (one per 16-token tile) when ksplit > 1.
+// per 16-token tile) and `counters` (one tile_counter per 16-token tile) when ksplit > 1.
 hipError_t launch_lora_small(const uint16_t *P, const uint16_t *Q, int64_t T, int64_t K, int r,
                              float scale, float *out_f32, uint16_t *out_bf16, int r_pad, float *partial,
                              uint32_t *counters, int ksplit, hipStream_t st);
@@ -46,10 +48,11 @@ bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T);
 // Work split of one contraction over 256 x 256 output tiles (gm x gn of them,
 // nk K steps of 64 each): tiles 0 .. full-1 run whole, one workgroup each; each
 // of the remaining `rem` tiles is cut into `split` K ranges run by separate
-// workgroups, whose float32 partial tiles (gemm_partial_floats in total, in
-// the workspace's shared scratch region) are summed by the last range to
-// finish. Chosen so that the chip's last round of tiles is not left mostly
-// idle; depends on the current device's compute-unit count.
+// workgroups, which store their float32 partial tiles (gemm_partial_floats in
+// total, in the workspace's shared scratch region), wait for each other
+// (bounded) and each sum a share of the tile's rows in range order. Chosen so
+// that the chip's last round of tiles is not left mostly idle; depends on the
+// current device's compute-unit count.
 struct GemmPlan {
   int gm, gn, nk, full, rem, split;
 };
@@ -70,13 +73,13 @@ constexpr int64_t kWideMinTokens = 65;
 // out[T, r] = P[T, K] . Q[r, K]^T (u = x A^T, v = dY B with Q = B^T); writes
 // out_f32 [T, r] (nullable) and out_bf16 = bf16(scale * out) [T, r_pad]
 // (nullable, zero columns r .. r_pad-1). Uses `partial`
-// (lora_tall_partial_floats) and `counters` (one per 64-token tile).
+// (lora_tall_partial_floats) and `counters` (one tile_counter per 64-token tile).
 hipError_t launch_lora_tall(const uint16_t *P, const uint16_t *Q, int64_t T, int64_t K, int r, int r_pad, float scale,
                             float *out_f32, uint16_t *out_bf16, float *partial, uint32_t *counters, hipStream_t st);
 size_t lora_tall_partial_floats(int64_t T, int64_t K, int r_pad);
 // X bf16 [T, D], Y float32 [T, R]. y_is_rows: C[R, D] = scale * Y^T X (dA);
 // otherwise C[D, R] = scale * X^T Y (dB). Uses `partial`
-// (lora_wgrad_partial_floats), `counters` (one per output tile) and sets *err
+// (lora_wgrad_partial_floats), `counters` (one tile_counter per output tile) and sets *err
 // if a bounded wait ran out.
 hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64_t D, int64_t R, bool y_is_rows,
                              float scale, float *C, float *partial, uint32_t *counters, uint32_t *err,

@@ -112,8 +112,10 @@ int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStr
  *   out  device bf16 [d_out, d_in], written in full; 16-byte aligned
  * out = bf16( w_hat + fl32(s * (B A)) ) with s = alpha / r in float32, B A
  * accumulated in float32 and one round-to-nearest-even at the end: within one
- * bf16 unit in the last place of the exactly rounded merge. The weight buffers
- * are only read. Errors: NULL, SHAPE (r outside 0..256 or r % 8 != 0), ALIGN,
+ * bf16 unit in the last place of the exactly rounded merge, plus the float32
+ * error of forming the sum (2^-24 (|w_hat| + (r+2) s sum_j |B_j||A_j|), which
+ * matters only where w_hat and s B A nearly cancel). The weight buffers are
+ * only read. Errors: NULL, SHAPE (r outside 0..256 or r % 8 != 0), ALIGN,
  * HIP (launch failure); nothing is written on a validation error.
  */
 int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
@@ -132,7 +134,7 @@ int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B,
  *          wait in the T <= 16 kernel timed out (the call's output is then
  *          unspecified). The rest of the workspace needs no initialisation.
  * T <= 16 runs one weight-streaming kernel (the adapter intermediate is formed
- * by the first workgroups of the same launch); larger T runs the MFMA GEMM.
+ * by the last workgroups of the same launch); larger T runs the MFMA GEMM.
  */
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A,
                   const uint16_t *B, int32_t r, float alpha, uint16_t *h, float *u_out, void *ws,
@@ -145,6 +147,10 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
  *   dA = (alpha/r) v^T x                 device f32 [r, d_in], nullable, overwritten
  *   dB = (alpha/r) dY^T u,  u = x A^T    device f32 [d_out, r], nullable, overwritten
  *   u_saved  device f32 [T, r] from qlora_forward's u_out, nullable (then recomputed)
+ *   x        needed only for dA, and for dB when u_saved is NULL: with a frozen A
+ *            (LoRA-FA, "8GB, 12GB, 16GB, 24GB GPU에서 몇 B 모델까지 LoRA 학습이
+ *            될까", section "LoRA 변형을 바꿔도 답이 같은 이유": the layer input
+ *            is not kept) pass x = NULL, dA = NULL and u_saved.
  * The codes/qscale/smax buffers are only read: no gradient flows into W.
  * With r == 0 only dX is produced (dA, dB must be NULL).
  */
