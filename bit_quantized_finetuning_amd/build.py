@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlora.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "lora_small.hip", "gemv.hip", "gemm.hip", "lora_grad.hip", "lora_wide.hip", "merge.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "lora_small.hip", "gemv.hip", "gemm.hip", "lora_grad.hip", "lora_wide.hip", "merge.hip", "adamw.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -181,6 +181,8 @@ const char *qlora_status_string(int status) {
     case QLORA_ERR_DTYPE: return "unknown dtype";
     case QLORA_ERR_HIP: return "HIP launch failed";
     case QLORA_ERR_INTERNAL: return "internal: the kernels' NF4 levels differ from the derived table";
+    case QLORA_ERR_MEMORY: return "a pointer is neither device memory nor pinned host memory";
+    case QLORA_ERR_VALUE: return "a hyperparameter is out of range (or step < 1)";
     default: return "unknown status";
   }
 }
@@ -228,6 +230,60 @@ int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B,
   const float sc = r > 0 ? alpha / (float)r : 0.f;
   return hip_status(launch_merge(W->codes, W->qscale, W->smax, W->d_out, W->d_in, r > 0 ? A : nullptr,
                                  r > 0 ? B : nullptr, r, sc, out, stream));
+}
+
+// A device-accessible address for a pointer into device memory or pinned host
+// memory; pageable host memory is refused (its lookup error is cleared so that
+// it does not surface from a later call).
+static int device_address(void *p, void **out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return QLORA_ERR_MEMORY;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged || at.isManaged) {
+    *out = p;
+    return QLORA_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return QLORA_ERR_MEMORY;
+    }
+    *out = d;
+    return QLORA_OK;
+  }
+  return QLORA_ERR_MEMORY;
+}
+
+int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, const float *grad, float *master,
+                     float *m, float *v, uint16_t *param, hipStream_t stream) {
+  if (!hp || !grad || !master || !m || !v) return QLORA_ERR_NULL;
+  if (n < 0) return QLORA_ERR_SHAPE;
+  if (step < 1 || !(hp->lr >= 0.f) || !(hp->beta1 >= 0.f && hp->beta1 < 1.f) ||
+      !(hp->beta2 >= 0.f && hp->beta2 < 1.f) || !(hp->eps > 0.f) || !(hp->weight_decay >= 0.f))
+    return QLORA_ERR_VALUE;
+  if (!aligned16(grad) || !aligned16(master) || !aligned16(m) || !aligned16(v) || (param && !aligned16(param)))
+    return QLORA_ERR_ALIGN;
+  if (n == 0) return QLORA_OK;
+  void *dg = nullptr, *dm = nullptr, *dmm = nullptr, *dv = nullptr, *dp = nullptr;
+  int s;
+  if ((s = device_address(const_cast<float *>(grad), &dg)) || (s = device_address(master, &dm)) ||
+      (s = device_address(m, &dmm)) || (s = device_address(v, &dv)) || (param && (s = device_address(param, &dp))))
+    return s;
+  AdamWArgs a;
+  a.lr = hp->lr;
+  a.b1 = hp->beta1;
+  a.b2 = hp->beta2;
+  a.one_minus_b1 = 1.f - hp->beta1;
+  a.one_minus_b2 = 1.f - hp->beta2;
+  a.eps = hp->eps;
+  a.decay = 1.f - hp->lr * hp->weight_decay;
+  a.c1 = (float)(1.0 - std::pow((double)hp->beta1, (double)step));
+  a.c2 = (float)(1.0 - std::pow((double)hp->beta2, (double)step));
+  return hip_status(launch_adamw(static_cast<const float *>(dg), static_cast<float *>(dm), static_cast<float *>(dmm),
+                                 static_cast<float *>(dv), static_cast<uint16_t *>(dp), n, a, stream));
 }
 
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,

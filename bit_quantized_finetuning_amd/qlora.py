@@ -7,7 +7,7 @@ there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
     qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_backward,
-    qlora_storage_bytes, qlora_workspace_bytes, qlora_nf4_codebook,
+    qlora_adamw_step, qlora_storage_bytes, qlora_workspace_bytes, qlora_nf4_codebook,
     qlora_nf4_thresholds, qlora_status_string
 """
 
@@ -52,6 +52,8 @@ _lib.qlora_dequantize.argtypes = [_W, ctypes.c_int, _vp, _vp]
 _lib.qlora_dequantize.restype = ctypes.c_int
 _lib.qlora_merge.argtypes = [_W, _vp, _vp, _i32, _f32, _vp, _vp]
 _lib.qlora_merge.restype = ctypes.c_int
+_lib.qlora_adamw_step.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.qlora_adamw_step.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
 _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -209,6 +211,31 @@ def qlora_merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, al
     _check(_lib.qlora_merge(ctypes.byref(cw), _ptr(A), _ptr(B), r, alpha, _ptr(out), _stream(out.device)),
            "qlora_merge")
     return out
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+def qlora_adamw_step(step: int, grad: torch.Tensor, master: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                     param: torch.Tensor | None = None, lr: float = 1e-4, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0, stream: torch.cuda.Stream | None = None):
+    """One AdamW step over float32 master/m/v (device or pinned host tensors, updated in place) from a device
+    float32 gradient; param (device bf16, optional) receives bf16(master). Enqueued on `stream` (default: the
+    current stream of grad's device)."""
+    for t in (grad, master, m, v):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("grad, master, m and v must be contiguous float32 tensors")
+    n = grad.numel()
+    if any(t.numel() != n for t in (master, m, v)) or (param is not None and param.numel() != n):
+        raise ValueError("all tensors must have the same number of elements")
+    if param is not None:
+        _bits(param)
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(grad.device)).cuda_stream)
+    _check(_lib.qlora_adamw_step(ctypes.byref(hp), step, n, _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
+                                 _ptr(param), st), "qlora_adamw_step")
 
 
 def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,

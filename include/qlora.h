@@ -54,8 +54,11 @@ typedef enum {
   QLORA_ERR_WORKSPACE = -4, /* ws_bytes < qlora_workspace_bytes(...)          */
   QLORA_ERR_DTYPE = -5,     /* unknown dtype enum                             */
   QLORA_ERR_HIP = -6,       /* a kernel launch failed                         */
-  QLORA_ERR_INTERNAL = -7   /* the levels compiled into the kernels differ from
+  QLORA_ERR_INTERNAL = -7,  /* the levels compiled into the kernels differ from
                                the table derived at load (never expected)      */
+  QLORA_ERR_MEMORY = -8,    /* a pointer is neither device memory nor pinned
+                               (hipHostMalloc) host memory                     */
+  QLORA_ERR_VALUE = -9      /* a hyperparameter is out of range                */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -158,6 +161,37 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
                    const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
                    const float *u_saved, uint16_t *dX, float *dA, float *dB, void *ws,
                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One AdamW step for adapter parameters whose optimizer state is paged out to
+ * host memory (first page, the paged-optimizer entry of section "메모리 회계":
+ * the adapters' Adam state m, v goes to CPU pinned memory and the update runs
+ * beside the backward on another stream). Per element, in float32, with
+ * decoupled weight decay (Loshchilov and Hutter's AdamW):
+ *     p <- p (1 - lr wd);  m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *     p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ *   hp      host struct: lr >= 0, 0 <= beta1, beta2 < 1, eps > 0, weight_decay >= 0
+ *   step    t >= 1 (the bias corrections are formed in float64, passed as float32)
+ *   n       number of elements (>= 0; 0 does nothing)
+ *   grad    device f32 [n] (e.g. qlora_backward's dA or dB)
+ *   master  f32 [n] float32 copy of the parameters, updated in place
+ *   m, v    f32 [n] first and second moments, updated in place
+ *   param   device bf16 [n], nullable: receives bf16(master) for the layer
+ * master, m and v may be device memory or pinned host memory (hipHostMalloc,
+ * e.g. torch pin_memory=True); the kernel reads and writes host memory in
+ * place. Every pointer 16-byte aligned. Errors: NULL, VALUE (hyperparameters,
+ * step < 1), SHAPE (n < 0), ALIGN, MEMORY (pageable host memory), HIP.
+ */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} qlora_adamw_hparams;
+
+int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, const float *grad, float *master,
+                     float *m, float *v, uint16_t *param, hipStream_t stream);
 
 /* Bytes of the quantized weight: n/2 + n/64 + 4*ceil(n/16384). */
 size_t qlora_storage_bytes(int64_t d_out, int64_t d_in);

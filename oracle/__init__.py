@@ -40,3 +40,4 @@ from .nf4 import (  # noqa: F401
     storage_bytes,
 )
 from .qlora import lora_forward, lora_backward, lora_merge, bf16_round_f64  # noqa: F401
+from .optim import adamw_step  # noqa: F401

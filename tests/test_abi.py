@@ -59,7 +59,7 @@ def test_workspace_bytes_positive_and_covers_buffers():
 
 
 def test_status_strings():
-    for s in (0, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DTYPE, -6):
+    for s in (0, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DTYPE, -6, -7, -8, -9):
         assert q.qlora_status_string(s)
     assert q.qlora_status_string(12345) == "unknown status"
 
@@ -124,3 +124,32 @@ def test_quantize_and_dequantize_reject_bad_arguments():
     assert q.lib.qlora_dequantize(ctypes.byref(w), 3, GOOD, None) == ERR_DTYPE
     assert q.lib.qlora_dequantize(ctypes.byref(w), 0, None, None) == ERR_NULL
     assert q.lib.qlora_dequantize(ctypes.byref(w), 0, BAD, None) == ERR_ALIGN
+
+
+def test_merge_rejects_bad_arguments():
+    w = _w()
+    assert q.lib.qlora_merge(ctypes.byref(w), GOOD, GOOD, 8, 16.0, None, None) == ERR_NULL
+    assert q.lib.qlora_merge(ctypes.byref(w), GOOD, GOOD, 12, 16.0, GOOD, None) == ERR_SHAPE   # r % 8
+    assert q.lib.qlora_merge(ctypes.byref(w), GOOD, None, 8, 16.0, GOOD, None) == ERR_NULL     # B missing
+    assert q.lib.qlora_merge(ctypes.byref(w), BAD, GOOD, 8, 16.0, GOOD, None) == ERR_ALIGN
+    assert q.lib.qlora_merge(ctypes.byref(_w(d_in=96)), GOOD, GOOD, 8, 16.0, GOOD, None) == ERR_SHAPE
+
+
+ERR_VALUE = -9
+
+
+def test_adamw_rejects_bad_arguments():
+    """Host-side validation runs before any pointer is looked up, so these need no GPU."""
+    def call(hp=None, step=1, n=16, grad=GOOD, master=GOOD, m=GOOD, v=GOOD, param=None):
+        hp = hp if hp is not None else q.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.0)
+        return q.lib.qlora_adamw_step(ctypes.byref(hp), step, n, grad, master, m, v, param, None)
+    assert q.lib.qlora_adamw_step(None, 1, 16, GOOD, GOOD, GOOD, GOOD, None, None) == ERR_NULL
+    assert call(grad=None) == ERR_NULL and call(v=None) == ERR_NULL
+    assert call(n=-1) == ERR_SHAPE
+    assert call(step=0) == ERR_VALUE
+    assert call(hp=q.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0.0)) == ERR_VALUE     # beta1 = 1
+    assert call(hp=q.AdamWHparams(1e-3, 0.9, 0.999, 0.0, 0.0)) == ERR_VALUE      # eps = 0
+    assert call(hp=q.AdamWHparams(-1e-3, 0.9, 0.999, 1e-8, 0.0)) == ERR_VALUE    # lr < 0
+    assert call(hp=q.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0.0)) == ERR_VALUE
+    assert call(m=BAD) == ERR_ALIGN and call(param=BAD) == ERR_ALIGN
+    assert call(n=0) == 0                                                          # nothing to do
