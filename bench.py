@@ -29,7 +29,12 @@ Other workloads are records, not the headline line:
   14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack
       (13.2 G parameters, generated on the device from a seeded generator);
   merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two
-      LLaMA-7B projections with r = 64.
+      LLaMA-7B projections with r = 64;
+  13b_paged_adamw  the 13b_4096tok step, timed without and with an AdamW update
+      of every A and B whose state (float32 master, m, v) sits in pinned host
+      memory; the update of a projection runs on a side stream beside the next
+      projection's forward and backward. Reported: the step with the update and
+      the throughput lost to it.
 """
 
 from __future__ import annotations
@@ -49,7 +54,7 @@ METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_quantize",
-                    "merge_llama7b"]
+                    "merge_llama7b", "13b_paged_adamw"]
 
 
 def parse():
@@ -63,6 +68,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true", help="skip the per-call-shape timings (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--paging", default="zerocopy", choices=["zerocopy", "dma"],
+                   help="13b_paged_adamw: update m, v in host memory in place, or copy each page to the device and back")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     return p.parse_args()
@@ -112,8 +119,10 @@ def main():
         return bench_merge(args, torch, q, synth, dev)
     if args.workload == "14b_quantize":
         return bench_quantize_stack(args, torch, q, synth, dev)
-    wl = synth.WORKLOADS[args.workload]
-    seed_cfg = synth.WORKLOAD_SEED[args.workload]
+    paged = args.workload == "13b_paged_adamw"
+    wname = "13b_4096tok" if paged else args.workload
+    wl = synth.WORKLOADS[wname]
+    seed_cfg = synth.WORKLOAD_SEED[wname]
     bw = bool(wl.backward)
     chunk = min(args.chunk, args.steps)
     nT = len(wl.tokens)
@@ -147,6 +156,29 @@ def main():
                             torch.empty(p.d_out, max(p.r, 1), dtype=torch.float32, device=dev),
                             torch.empty(T, max(p.r, 1), dtype=torch.float32, device=dev))
         projs.append((p, copies, xs, dys, outs, grads))
+    # paged AdamW state per projection and copy: the Adam moments m, v of A and B in pinned host memory, the
+    # float32 master copy on the device
+    opt_state = {}
+    opt_stream = torch.cuda.Stream(dev) if paged else None  # default priority
+    if paged:
+        for pi, (p, copies, *_rest) in enumerate(projs):
+            for ci, (wc, A, B) in enumerate(copies):
+                if A is None:
+                    continue
+                st = []
+                for t in (A, B):
+                    master = t.float()
+                    st.append((t, master, torch.zeros(t.numel(), dtype=torch.float32).pin_memory(),
+                               torch.zeros(t.numel(), dtype=torch.float32).pin_memory()))
+                opt_state[(pi, ci)] = st
+    # DMA paging: one device page (m, v) sized for the largest parameter, reused in turn on the update stream
+    # (its copies and kernels run in order there)
+    page = None
+    if paged and args.paging == "dma" and opt_state:
+        nmax = max(st[1].numel() for sts in opt_state.values() for st in sts)
+        page = [torch.empty(nmax, dtype=torch.float32, device=dev) for _ in range(2)]
+    opt_on = [False]
+    opt_pending = {}
     # one workspace large enough for every call, allocated (zeroed) before any capture
     ws_need = max(q.qlora_workspace_bytes(p.d_out, p.d_in, T, p.r) for p, *_ in projs for T in wl.tokens)
     q.workspace(dev, ws_need)
@@ -156,58 +188,107 @@ def main():
              for p, copies, xs, dys, outs, grads in projs for ti, T in enumerate(wl.tokens)]
 
     def run_call(p, copies, x, dy, h, g, T, ti, k):
-        wc, A, B = copies[k % len(copies)]
+        ci = k % len(copies)
+        wc, A, B = copies[ci]
         if not bw:
             q.qlora_forward(wc, x, A, B, p.alpha, h=h)
             return
+        pi = next(i for i, pr in enumerate(projs) if pr[0] is p)
+        if opt_on[0] and (pi, ci) in opt_pending:
+            # the previous update of these parameters must land before the forward reads them
+            torch.cuda.current_stream(dev).wait_event(opt_pending.pop((pi, ci)))
         dX, dA, dB, u = g
         ur = u if p.r > 0 else None
         q.qlora_forward(wc, x, A, B, p.alpha, h=h, u=ur)
         q.qlora_backward(wc, x, dy, A, B, p.alpha, u_saved=ur, dX=dX, dA=dA if p.r > 0 else None,
                          dB=dB if p.r > 0 else None)
+        if opt_on[0] and (pi, ci) in opt_state:
+            ready = torch.cuda.Event()
+            ready.record(torch.cuda.current_stream(dev))
+            opt_stream.wait_event(ready)
+            for (t, master, m, v), grad in zip(opt_state[(pi, ci)], (dA, dB)):
+                if page is None:  # zero-copy: the kernel updates the state in host memory
+                    q.qlora_adamw_step(1, grad.view(-1), master.view(-1), m.view(-1), v.view(-1), t.view(-1),
+                                       lr=1e-4, weight_decay=0.01, stream=opt_stream)
+                    continue
+                n_el = master.numel()
+                dmm, dv = (b[:n_el] for b in page)
+                with torch.cuda.stream(opt_stream):
+                    for d, h in ((dmm, m), (dv, v)):
+                        d.copy_(h, non_blocking=True)
+                q.qlora_adamw_step(1, grad.view(-1), master.view(-1), dmm, dv, t.view(-1), lr=1e-4, weight_decay=0.01,
+                                   stream=opt_stream)
+                with torch.cuda.stream(opt_stream):
+                    for d, h in ((dmm, m), (dv, v)):
+                        h.copy_(d, non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(opt_stream)
+            opt_pending[(pi, ci)] = done
 
     def run_steps(s0, n):
         for s in range(s0, s0 + n):
             for c in calls:
                 run_call(*c, s * nT + c[-1])
+        if opt_on[0]:
+            # join the update stream (also closes a graph capture's fork)
+            torch.cuda.current_stream(dev).wait_stream(opt_stream)
+            opt_pending.clear()
 
     stream = torch.cuda.current_stream(dev)
-    for s in range(max(args.warmup, 1)):
-        run_steps(s % chunk, 1)
-    torch.cuda.synchronize()
 
-    # ---- graphs: one of `chunk` steps, and one of the remainder
-    graphs = {}
-    if not args.no_graph:
-        side = torch.cuda.Stream(dev)  # default priority
-        for n in sorted({chunk, args.steps % chunk} - {0}):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                run_steps(0, n)
-            graphs[n] = g
+    def measure():
+        """Warm up, capture the step graphs, replay once, then time exactly args.steps steps (ms)."""
+        for s in range(max(args.warmup, 1)):
+            run_steps(s % chunk, 1)
         torch.cuda.synchronize()
-        for n, g in graphs.items():       # one untimed replay of each
-            g.replay()
-        torch.cuda.synchronize()
-
-    def timed(K):
+        # ---- graphs: one of `chunk` steps, and one of the remainder
+        graphs = {}
+        if not args.no_graph:
+            side = torch.cuda.Stream(dev)  # default priority
+            for n in sorted({chunk, args.steps % chunk} - {0}):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    run_steps(0, n)
+                graphs[n] = g
+            torch.cuda.synchronize()
+            for n, g in graphs.items():       # one untimed replay of each
+                g.replay()
+            torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
         if graphs:
-            for _ in range(K // chunk):
+            for _ in range(args.steps // chunk):
                 graphs[chunk].replay()
-            if K % chunk:
-                graphs[K % chunk].replay()
+            if args.steps % chunk:
+                graphs[args.steps % chunk].replay()
         else:
-            run_steps(0, K)
+            run_steps(0, args.steps)
         t1.record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
+        return t0.elapsed_time(t1), bool(graphs)
 
-    ms_total = timed(args.steps)
+    paged_info = None
+    if paged:
+        ms_off, _ = measure()           # the step alone
+        opt_on[0] = True
+        ms_total, have_graphs = measure()  # the step with the paged update
+        opt_on[0] = False
+        n_opt = sum(st[0].numel() for sts in opt_state.values() for st in sts) // max(len(projs[0][1]), 1)
+        paged_info = {"ms_per_step_without_optimizer": round(ms_off / args.steps, 5),
+                      "optimizer_throughput_loss_pct": round(100.0 * (1.0 - ms_off / ms_total), 2),
+                      "optimizer": "AdamW (lr 1e-4, wd 0.01): m and v of every A and B in pinned host memory, float32 "
+                                   "master on the device, updated by qlora_adamw_step on a side stream beside the next "
+                                   "projection; "
+                                   + ("each state page copied to the device and back by DMA around the update"
+                                      if args.paging == "dma" else "the kernel reads and writes host memory in place"),
+                      "adapter_params_per_step": n_opt,
+                      "host_link_bytes_per_step": 16 * n_opt}
+    else:
+        ms_total, have_graphs = measure()
     ms_step = ms_total / args.steps
+    graphs = {chunk: None} if have_graphs else {}
 
     fb = sum(fwd_bytes(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls)
     ff = sum(fwd_flops(p.d_out, p.d_in, p.r, T) for p, *_, T, _ in calls)
@@ -275,6 +356,9 @@ def main():
         "per_call": per_call,
         "cpu_baseline": cpu,
     }
+    if paged_info:
+        line["config"]["workload"] = wl.description + ", with a paged AdamW update of every A and B"
+        line["config"].update(paged_info)
     print(json.dumps(line), flush=True)
 
 
