@@ -17,8 +17,19 @@
 //     v <- b2 v + (1 - b2) g^2
 //     p <- p - lr (m / c1) / (sqrt(v / c2) + eps),  c1 = 1 - b1^t, c2 = 1 - b2^t
 // in float32 (c1 and c2 are formed on the host in float64 and passed rounded).
-// The kernel is bound by the host link when the state is in host memory (16
-// bytes read and 12 written per element over it) and by HBM otherwise.
+// The kernel is bound by the host link when the state is in host memory (8
+// bytes read and 8 written per element for m and v there, 16 and 12 with the
+// master copy too) and by HBM otherwise.
+//
+// Grid: with all operands in device memory, enough workgroups to fill the chip
+// (HBM bound). With state in host memory the step is link bound and meant to
+// run beside the backward's kernels on another stream; there a few workgroups
+// already keep enough requests in flight to saturate the link (32 x 256 lanes
+// x 16 bytes per state stream per round trip), while every extra one occupies a
+// CU slot, stalled on host latency, that the concurrent GEMM tiles wait for. On
+// the 13B projections at 4096 tokens the cost of the paged update to the step
+// fell from about 19 % with up to 2048 workgroups to about 12 % with 32 (16 and
+// 8 were no better; more loads in flight per lane did not help either).
 #include "kernels.h"
 
 namespace qlora {
@@ -67,11 +78,15 @@ __global__ __launch_bounds__(256) void k_adamw(const float *__restrict__ grad, f
   }
 }
 
+constexpr int64_t kAdamWBlocksDevice = 2048;
+constexpr int64_t kAdamWBlocksHost = 32;
+
 hipError_t launch_adamw(const float *grad, float *master, float *m, float *v, uint16_t *param, int64_t n,
-                        const AdamWArgs &a, hipStream_t st) {
+                        const AdamWArgs &a, bool host_state, hipStream_t st) {
+  const int64_t cap = host_state ? kAdamWBlocksHost : kAdamWBlocksDevice;
   int64_t blocks = (n / 4 + 255) / 256;
   if (blocks < 1) blocks = 1;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > cap) blocks = cap;
   k_adamw<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(grad, master, m, v, param, n, a);
   return hipGetLastError();
 }

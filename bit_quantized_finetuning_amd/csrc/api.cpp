@@ -233,9 +233,9 @@ int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B,
 }
 
 // A device-accessible address for a pointer into device memory or pinned host
-// memory; pageable host memory is refused (its lookup error is cleared so that
-// it does not surface from a later call).
-static int device_address(void *p, void **out) {
+// memory (*host is set for the latter); pageable host memory is refused (its
+// lookup error is cleared so that it does not surface from a later call).
+static int device_address(void *p, void **out, bool *host) {
   hipPointerAttribute_t at;
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
     (void)hipGetLastError();
@@ -243,6 +243,7 @@ static int device_address(void *p, void **out) {
   }
   if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged || at.isManaged) {
     *out = p;
+    *host = false;
     return QLORA_OK;
   }
   if (at.type == hipMemoryTypeHost) {
@@ -252,6 +253,7 @@ static int device_address(void *p, void **out) {
       return QLORA_ERR_MEMORY;
     }
     *out = d;
+    *host = true;
     return QLORA_OK;
   }
   return QLORA_ERR_MEMORY;
@@ -268,9 +270,11 @@ int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, con
     return QLORA_ERR_ALIGN;
   if (n == 0) return QLORA_OK;
   void *dg = nullptr, *dm = nullptr, *dmm = nullptr, *dv = nullptr, *dp = nullptr;
+  bool hg = false, hm = false, hmm = false, hv = false, hp_ = false;
   int s;
-  if ((s = device_address(const_cast<float *>(grad), &dg)) || (s = device_address(master, &dm)) ||
-      (s = device_address(m, &dmm)) || (s = device_address(v, &dv)) || (param && (s = device_address(param, &dp))))
+  if ((s = device_address(const_cast<float *>(grad), &dg, &hg)) || (s = device_address(master, &dm, &hm)) ||
+      (s = device_address(m, &dmm, &hmm)) || (s = device_address(v, &dv, &hv)) ||
+      (param && (s = device_address(param, &dp, &hp_))))
     return s;
   AdamWArgs a;
   a.lr = hp->lr;
@@ -283,7 +287,8 @@ int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, con
   a.c1 = (float)(1.0 - std::pow((double)hp->beta1, (double)step));
   a.c2 = (float)(1.0 - std::pow((double)hp->beta2, (double)step));
   return hip_status(launch_adamw(static_cast<const float *>(dg), static_cast<float *>(dm), static_cast<float *>(dmm),
-                                 static_cast<float *>(dv), static_cast<uint16_t *>(dp), n, a, stream));
+                                 static_cast<float *>(dv), static_cast<uint16_t *>(dp), n, a,
+                                 hg || hm || hmm || hv || hp_, stream));
 }
 
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,

@@ -20,12 +20,13 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const 
 // adamw.hip: one AdamW step over n float32 elements (see the kernel file).
 // grad, master, m, v are device-accessible addresses (pinned host memory
 // mapped for the device, or device memory); param (nullable, device) receives
-// bf16(master).
+// bf16(master). host_state: some operand is in host memory, so the step is
+// bound by the host link rather than HBM.
 struct AdamWArgs {
   float lr, b1, b2, one_minus_b1, one_minus_b2, eps, decay, c1, c2;
 };
 hipError_t launch_adamw(const float *grad, float *master, float *m, float *v, uint16_t *param, int64_t n,
-                        const AdamWArgs &a, hipStream_t st);
+                        const AdamWArgs &a, bool host_state, hipStream_t st);
 
 // merge.hip: out[d_out, d_in] = bf16(W_hat + scale B A), A [r, d_in], B [d_out, r] bf16 (r may be 0).
 hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out, int64_t d_in,
