@@ -38,6 +38,9 @@ from .nf4 import (  # noqa: F401
     dequant_scales,
     dequantize,
     storage_bytes,
+    quantize_absmax,
+    dequantize_absmax,
+    storage_bytes_absmax,
 )
 from .qlora import lora_forward, lora_backward, lora_merge, bf16_round_f64  # noqa: F401
 from .optim import adamw_step  # noqa: F401

@@ -21,6 +21,11 @@ What is computed, in the pages' order:
   5. dequantization back to bf16 for the matmul -- [48GB] "Each weight takes
      4 bits ... restored to bf16 before participating in matrix multiplication".
 
+The absmax-only storage (steps 1-3 and 5 without step 4) is the variant the
+pages price at 4.5 bits per parameter: every block keeps its float32 scale
+([QLoRA-65B] "메모리 회계", NF4 paragraph; double quantization then takes it
+to 4.13). quantize_absmax / dequantize_absmax / storage_bytes_absmax.
+
 Readings taken where the pages are silent (each also listed in the design doc):
   * codebook: 8 positive levels at Phi^-1(1/2 + (p-1/2) j/8), j=1..8, 7 negative
     levels at -Phi^-1(1/2 + (p-1/2) j/7), j=1..7, and 0, with
@@ -237,6 +242,41 @@ def dequantize(codes: np.ndarray, q2: np.ndarray, S: np.ndarray, d_out: int, d_i
     sh = dequant_scales(q2, S)
     w = (c[q].reshape(-1, BLOCK) * sh[:, None]).astype(np.float32).reshape(d_out, d_in)
     return w, bf16_round(w)
+
+
+def quantize_absmax(W: np.ndarray):
+    """Quantize W [d_out, d_in] to NF4 with the float32 absmax of every block kept as is (no double quant).
+
+    Returns (codes uint8 [n/2], s float32 [n/64]). The codes are those of quantize(): they come from the
+    exact block scale either way; only the storage of the scale differs.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    assert W.ndim == 2 and W.shape[1] % BLOCK == 0, "d_in must be a multiple of 64"
+    w = W.reshape(-1)
+    s = block_absmax(w)
+    wb = w.reshape(-1, BLOCK)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        xn = (wb / s[:, None]).astype(np.float32)      # IEEE float32 divide
+    xn[s == 0, :] = 0.0
+    return pack_codes(nearest_level(xn).reshape(-1)), s
+
+
+def dequantize_absmax(codes: np.ndarray, s: np.ndarray, d_out: int, d_in: int):
+    """Restore W from absmax-only storage: w_hat_i = fl32(c(q_i) * s_k), then bf16.
+
+    Returns (float32 w_hat [d_out, d_in], float32 holding the bf16-rounded w_hat).
+    """
+    c = nf4_codebook()
+    q = unpack_codes(codes)
+    s = np.asarray(s, dtype=np.float32)
+    w = (c[q].reshape(-1, BLOCK) * s[:, None]).astype(np.float32).reshape(d_out, d_in)
+    return w, bf16_round(w)
+
+
+def storage_bytes_absmax(d_out: int, d_in: int) -> int:
+    """Bytes of the absmax-only storage: n/2 (codes) + 4 n/64 (one float32 scale per block)."""
+    n = d_out * d_in
+    return n // 2 + 4 * (n // BLOCK)
 
 
 def storage_bytes(d_out: int, d_in: int) -> int:

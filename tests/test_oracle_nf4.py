@@ -340,3 +340,78 @@ def test_storage_bytes_layout():
     assert oracle.storage_bytes(11008, 4096) == 22544384 + 704512 + 4 * 2752
     # d_in = 5120: groups straddle rows, last group full
     assert oracle.storage_bytes(5120, 5120) == 13107200 + 409600 + 6400
+
+
+# ---------------------------------------------------------------------------
+# absmax-only storage (no double quantization): 4.5 bits per parameter
+# ---------------------------------------------------------------------------
+
+def test_absmax_storage_is_4_5_bits():
+    g = _golden()
+    for d_out, d_in in ((4096, 4096), (11008, 4096), (16, 64), (80, 320)):
+        n = d_out * d_in
+        assert 8 * oracle.storage_bytes_absmax(d_out, d_in) / n == g["bits_per_param_absmax_only"]["value"]
+
+
+def test_absmax_quantize_bruteforce_tiny():
+    rs = np.random.default_rng(8)
+    W = (rs.standard_normal((4, 192)) * 0.02).astype(np.float32)
+    W[1, 64:128] = 0.0                                  # a zero block
+    W[2, 0:64] = np.linspace(-3, 5, 64)                 # spread block
+    W[3, 128:192] = -np.abs(W[3, 128:192])              # all-negative block
+    codes, s = oracle.quantize_absmax(W)
+    assert list(oracle.unpack_codes(codes)) == _brute_quantize(W)
+    flat = [float(v) for v in W.reshape(-1)]
+    brute_s = [max(abs(v) for v in flat[64 * k:64 * k + 64]) for k in range(len(flat) // 64)]
+    assert s.dtype == np.float32 and list(s.astype(np.float64)) == brute_s
+    # same codes as the double-quant storage: the codes never see the re-coded scale
+    assert np.array_equal(codes, oracle.quantize(W)[0])
+
+
+def test_absmax_restore_is_lossless_on_scaled_levels():
+    """Weights that are exactly a level times a power of two come back unchanged (no scale re-coding)."""
+    c = oracle.nf4_codebook()
+    rs = np.random.default_rng(9)
+    rows = []
+    for e in (-12, -7, 0, 3):
+        idx = rs.integers(0, 16, 64)
+        idx[rs.integers(0, 64)] = 15 if e % 2 else 0   # the block's absmax is 2^e
+        rows.append(c[idx] * np.float32(2.0 ** e))
+    W = np.stack(rows).astype(np.float32).reshape(4, 64)
+    codes, s = oracle.quantize_absmax(W)
+    assert np.array_equal(s, np.float32(2.0) ** np.array([-12, -7, 0, 3], dtype=np.float32))
+    w, wb = oracle.dequantize_absmax(codes, s, 4, 64)
+    assert np.array_equal(w, W)
+    tb = torch.from_numpy(w).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(wb, tb)
+
+
+def test_absmax_restore_error_within_half_the_level_gap():
+    """|w_hat - w| <= s * (largest gap between adjacent levels) / 2, plus the float32 products' rounding."""
+    c = oracle.nf4_codebook().astype(np.float64)
+    half_gap = np.max(np.diff(c)) / 2
+    rs = np.random.default_rng(10)
+    W = (rs.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    W[3, :64] = 0.0
+    codes, s = oracle.quantize_absmax(W)
+    w, _ = oracle.dequantize_absmax(codes, s, 32, 512)
+    err = np.abs(w.astype(np.float64) - W.astype(np.float64)).reshape(-1, 64)
+    sk = s.astype(np.float64)[:, None]
+    assert np.all(err <= sk * (half_gap + 2.0 ** -23))
+    assert np.all(w.reshape(-1, 64)[3 * 8] == 0)
+    # no worse than double quantization, whose scale carries an extra error of up to S/256
+    codes2, q2, S = oracle.quantize(W)
+    w2, _ = oracle.dequantize(codes2, q2, S, 32, 512)
+    assert np.linalg.norm(w - W) <= np.linalg.norm(w2 - W)
+
+
+def test_absmax_restore_matches_torch_float32_product():
+    rs = np.random.default_rng(12)
+    W = (rs.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    codes, s = oracle.quantize_absmax(W)
+    w, wb = oracle.dequantize_absmax(codes, s, 16, 256)
+    c = torch.from_numpy(oracle.nf4_codebook())
+    q = torch.from_numpy(oracle.unpack_codes(codes).astype(np.int64)).view(-1, 64)
+    ref = (c[q] * torch.from_numpy(s)[:, None]).view(16, 256)
+    assert torch.equal(torch.from_numpy(w), ref)
+    assert torch.equal(torch.from_numpy(wb), ref.to(torch.bfloat16).float())
