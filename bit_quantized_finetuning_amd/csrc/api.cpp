@@ -91,11 +91,13 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int validate_weight(const qlora_nf4_weight *W) {
   if (!literals_match()) return QLORA_ERR_INTERNAL;
-  if (!W || !W->codes || !W->qscale || !W->smax) return QLORA_ERR_NULL;
+  if (!W || !W->codes || !W->smax) return QLORA_ERR_NULL;  // qscale NULL: absmax-only storage
   if (W->d_out < 1 || W->d_in < QLORA_BLOCK || W->d_in % QLORA_BLOCK != 0 || W->d_out % 16 != 0)
     return QLORA_ERR_SHAPE;
   if (W->d_out > kMaxDim || W->d_in > kMaxDim) return QLORA_ERR_SHAPE;
-  if (!aligned16(W->codes) || !aligned16(W->qscale) || !aligned16(W->smax)) return QLORA_ERR_ALIGN;
+  // absmax-only storage: the kernels address the float32 block scales as one buffer range
+  if (!W->qscale && W->d_out * W->d_in / QLORA_BLOCK * 4 >= ((int64_t)1 << 31)) return QLORA_ERR_SHAPE;
+  if (!aligned16(W->codes) || (W->qscale && !aligned16(W->qscale)) || !aligned16(W->smax)) return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
 
@@ -191,6 +193,12 @@ size_t qlora_storage_bytes(int64_t d_out, int64_t d_in) {
   if (d_out < 1 || d_in < 1) return 0;
   const int64_t n = d_out * d_in, nb = n / QLORA_BLOCK;
   return (size_t)(n / 2 + nb + 4 * ceil_div(nb, QLORA_GROUP));
+}
+
+size_t qlora_storage_bytes_absmax(int64_t d_out, int64_t d_in) {
+  if (d_out < 1 || d_in < 1) return 0;
+  const int64_t n = d_out * d_in;
+  return (size_t)(n / 2 + 4 * (n / QLORA_BLOCK));
 }
 
 size_t qlora_workspace_bytes(int64_t d_out, int64_t d_in, int64_t T, int32_t r) {

@@ -18,6 +18,20 @@ namespace qlora {
 
 constexpr int kBlock = 64;
 constexpr int kGroup = 256;
+// Where a weight keeps its block scales. Double quantization (the default): an
+// 8-bit code q2 per block and a float32 S per group of 256 blocks, the scale of
+// block k being restore_scale(q2[k], S[k >> 8]). Absmax-only storage (4.5 bits
+// per weight, the variant without double quantization on the first page,
+// section "메모리 회계"): the float32 block absmax s_k itself, read as
+// S[k >> 0] with the code taken as 256, for which restore_scale gives
+// fl32(1 * s_k) = s_k exactly. Kernels receive the shift (kDqShift or 0); with
+// shift 0 their q2 buffer range is empty, so its loads return 0, and
+// q2_or(0) = 256 is OR-ed into the code where it is used.
+constexpr int kDqShift = 8;  // log2(kGroup)
+__host__ __device__ inline uint32_t q2_or(int sshift) { return sshift ? 0u : 256u; }
+__host__ __device__ inline int64_t scale_words(int64_t nblocks, int sshift) {
+  return (nblocks + ((int64_t)1 << sshift) - 1) >> sshift;
+}
 // Split reductions count arriving workgroups per output tile in a fixed region
 // at the start of the workspace (zero before first use, left zero by every
 // kernel). Each tile's counter has a 128-byte line of its own: the workgroups

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
                                                        const uint16_t *__restrict__ B, int r,
                                                        uint16_t *__restrict__ h, float *__restrict__ partial,
                                                        uint32_t *__restrict__ counters, int gn, int full,
-                                                       int split) {
+                                                       int split, int sshift) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [2][kTile] activation ring
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, ml = lane & 31;
@@ -411,8 +411,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   const int64_t nrows = d_out - n0 < kBN ? d_out - n0 : kBN;
   const rsrc_t xr = make_rsrc(x + m0 * d_in, mrows * d_in * 2);
   const rsrc_t cr = make_rsrc(codes + n0 * (d_in / 2), nrows * (d_in / 2));
-  const rsrc_t qr = make_rsrc(qscale + n0 * KB, nrows * KB);
-  const rsrc_t sr = make_rsrc(smax, ((d_out * KB + kGroup - 1) / kGroup) * 4);
+  // absmax-only storage (sshift 0): an empty q2 range (loads return 0) and one scale per block
+  const rsrc_t qr = make_rsrc(qscale + n0 * KB, sshift ? nrows * KB : 0);
+  const rsrc_t sr = make_rsrc(smax, scale_words(d_out * KB, sshift) * 4);
+  const uint32_t q2o = q2_or(sshift);
 
   int aoff[4];
 #pragma unroll
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
     for (int j = 0; j < 2; ++j) {
       C.c[j] = bld16s(cr, coff[j], kc * (kBlock / 2));
       C.q2[j] = bld8s(qr, qoff[j], kc);
-      C.S[j] = __uint_as_float(bld32(sr, ((blk0[j] + (uint32_t)kc) >> 8) * 4u));
+      C.S[j] = __uint_as_float(bld32(sr, ((blk0[j] + (uint32_t)kc) >> sshift) * 4u));
     }
   };
 
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   for (int j = 0; j < 2; ++j) {
     TableBuild tb;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j], C0.S[j], t[j]);
+    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j] | q2o, C0.S[j], t[j]);
     fb[0][j] = expand8(t[j], C0.c[j][0]);
   }
 #pragma unroll
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
           if (q == 0) issue_codes(kt + 2, Ccur);
           if (q >= 1 && q <= 6) {
             const int jj = (q - 1) / 3;
-            tb.run((q - 1) % 3, Cnext.q2[jj], Cnext.S[jj], t[jj]);
+            tb.run((q - 1) % 3, Cnext.q2[jj] | q2o, Cnext.S[jj], t[jj]);
           }
           if (q == 7) wait_barrier<6>();
           if (q >= 8) {
@@ -565,9 +567,9 @@ struct DxRestore {
   Nf4Planes t;
   Expand ex;
   u32x4 v;
-  __device__ __forceinline__ void run(int k, const DxCodes &C, uint8_t *tile, uint32_t wxor) {
+  __device__ __forceinline__ void run(int k, const DxCodes &C, uint8_t *tile, uint32_t wxor, uint32_t q2o) {
     if (k < 3) {
-      tb.run(k, C.q2, C.S, t);
+      tb.run(k, C.q2 | q2o, C.S, t);
     } else if (k < 35) {
       const int m = (k - 3) >> 2, ph = (k - 3) & 3;
       const uint32_t w = m < 4 ? C.c0[m & 3] : C.c1[m & 3];
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
                                                       const uint16_t *__restrict__ A, int r,
                                                       uint16_t *__restrict__ dX, float *__restrict__ partial,
                                                       uint32_t *__restrict__ counters, int gn, int full,
-                                                      int split) {
+                                                      int split, int sshift) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t *ring = smem;                                             // [2][kTile]     dY tiles [t][o]
   uint8_t *Bt = smem + 2 * kTile;                                   // [2][kWTile]    W_hat tiles [o][i]
@@ -634,15 +636,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   const int wo = 8 * ((tid >> 4) & 7) + (tid & 7), wb = 2 * (tid >> 7) + ((tid >> 3) & 1);
   const uint32_t wxor = (uint32_t)(wo * kWRow + ((8 * wb ^ wswz(wo)) << 4));
   const int64_t kblk = n0 / kBlock + wb;
+  const uint32_t q2o = q2_or(sshift);
   auto issue_codes = [&](int kt, DxCodes &C) {
     // weight rows k0..k0+63: ranges rebased per K tile (32-bit offsets stay small for any weight size)
     const int64_t k0 = (int64_t)kt * kBK;
     const int64_t orows = kt < nk ? (d_out - k0 < kBK ? d_out - k0 : kBK) : 0;
     const int64_t kr = kt < nk ? k0 : 0;
     const rsrc_t crr = make_rsrc(codes + kr * (d_in / 2), orows * (d_in / 2));
-    const rsrc_t qrr = make_rsrc(qscale + kr * KB, orows * KB);
-    const int64_t gb = (kr * KB) >> 8;  // first group of the tile's rows
-    const rsrc_t srr = make_rsrc(smax + gb, ((d_out * KB + kGroup - 1) / kGroup - gb) * 4);
+    const rsrc_t qrr = make_rsrc(qscale + kr * KB, sshift ? orows * KB : 0);
+    const int64_t gb = (kr * KB) >> sshift;  // first scale word of the tile's rows
+    const rsrc_t srr = make_rsrc(smax + gb, (scale_words(d_out * KB, sshift) - gb) * 4);
     // Rows past the tile's end fall outside the ranges and restore to zero
     // (scale code 0). Blocks past d_in (kblk >= KB) read the next row's
     // blocks: finite values that reach only output columns past d_in, which
@@ -651,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
     C.c0 = bld16(crr, lblk * 32u);
     C.c1 = bld16(crr, lblk * 32u + 16u);
     C.q2 = bld8(qrr, lblk);
-    C.S = __uint_as_float(bld32(srr, (uint32_t)((((kr * KB) & (kGroup - 1)) + lblk) >> 8) * 4u));
+    C.S = __uint_as_float(bld32(srr, (uint32_t)((((kr * KB) & ((1 << sshift) - 1)) + lblk) >> sshift) * 4u));
   };
 
   f32x16 acc[8][2];
@@ -667,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   {
     DxRestore rs;
 #pragma unroll
-    for (int k = 0; k < 35; ++k) rs.run(k, C0, Bt, wxor);
+    for (int k = 0; k < 35; ++k) rs.run(k, C0, Bt, wxor, q2o);
   }
   wait_barrier<4>();
 #pragma unroll
@@ -700,7 +703,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
         if (s < 3) {
           if (q < 8) fa[(s + 1) & 1][q] = *reinterpret_cast<const u32x4 *>(cur + aoff[s + 1] + 4096 * q);
           if (q == 8 || q == 10) fb[(s + 1) & 1][(q - 8) >> 1] = frag_b(bcur, s + 1, (q - 8) >> 1);
-          rs.run(16 * s + q, Cnext, bnxt, wxor);
+          rs.run(16 * s + q, Cnext, bnxt, wxor, q2o);
         } else {
           if (q == 7) wait_barrier<4>();
           if (q >= 8) fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
@@ -829,8 +832,10 @@ hipError_t launch_gemm_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
   const GemmPlan p = gemm_plan(T, d_out, d_in / kBlock);
   if (p.rem > kMaxTileCounters) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(p.full + p.rem * p.split);
-  k_gemm_fwd<<<dim3(grid), dim3(kThreads), kFwdLds, st>>>(codes, qscale, smax, d_out, d_in, x, T, su, r_pad, B, r,
-                                                            h, partial, counters, p.gn, p.full, p.split);
+  // absmax-only storage: no scale codes (the kernel's q2 range is then empty)
+  k_gemm_fwd<<<dim3(grid), dim3(kThreads), kFwdLds, st>>>(codes, qscale ? qscale : codes, smax, d_out, d_in, x, T, su,
+                                                            r_pad, B, r, h, partial, counters, p.gn, p.full, p.split,
+                                                            qscale ? kDqShift : 0);
   return hipGetLastError();
 }
 
@@ -843,8 +848,9 @@ hipError_t launch_gemm_dx(const uint8_t *codes, const uint8_t *qscale, const flo
   const GemmPlan p = gemm_plan(T, d_in, (d_out + kBK - 1) / kBK);
   if (p.rem > kMaxTileCounters) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(p.full + p.rem * p.split);
-  k_gemm_dx<<<dim3(grid), dim3(kThreads), kDxLds, st>>>(codes, qscale, smax, d_out, d_in, dY, T, sv, r_pad, A, r,
-                                                          dX, partial, counters, p.gn, p.full, p.split);
+  k_gemm_dx<<<dim3(grid), dim3(kThreads), kDxLds, st>>>(codes, qscale ? qscale : codes, smax, d_out, d_in, dY, T, sv,
+                                                          r_pad, A, r, dX, partial, counters, p.gn, p.full, p.split,
+                                                          qscale ? kDqShift : 0);
   return hipGetLastError();
 }
 

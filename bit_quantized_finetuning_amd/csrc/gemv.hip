@@ -75,12 +75,12 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ qscale, const float *__restrict__ smax,
     int d_out, int d_in, const uint16_t *__restrict__ x, int T, const uint16_t *__restrict__ A,
     const uint16_t *__restrict__ B, int r, int r_pad, float scale, uint16_t *__restrict__ h,
-    float *__restrict__ u_out, uint64_t *__restrict__ uex, uint32_t *__restrict__ sync) {
+    float *__restrict__ u_out, uint64_t *__restrict__ uex, uint32_t *__restrict__ sync, int sshift) {
   // All kernel arguments in one scalar-memory round trip (left alone, the
   // compiler fetches them in dependent batches at first use).
   asm volatile("; kernel arguments" ::"s"(codes), "s"(qscale), "s"(smax), "s"(d_out), "s"(d_in), "s"(x), "s"(T),
                "s"(A), "s"(B), "s"(r), "s"(r_pad), "s"(scale), "s"(h), "s"(u_out), "s"(uex), "s"(sync),
-               "s"(gridDim.x));
+               "s"(sshift), "s"(gridDim.x));
   constexpr int kThreads = 64 * kW;
   extern __shared__ __attribute__((aligned(16))) uint16_t x_l[];  // [T][d_in + kXPad] when kXL
   __shared__ float red[kW][256];
@@ -102,8 +102,10 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   const int mseg = NS > wv ? (NS - wv + kW - 1) / kW : 0;  // my segments per row tile
   const int nblocks = d_out * KB;
   const rsrc_t cr = make_rsrc(codes, (int64_t)nblocks * (kBlock / 2));
-  const rsrc_t qr = make_rsrc(qscale, nblocks);
-  const rsrc_t sr = make_rsrc(smax, (int64_t)((nblocks + kGroup - 1) / kGroup) * 4);
+  // absmax-only storage (sshift 0): an empty q2 range (loads return 0) and one scale per block
+  const rsrc_t qr = make_rsrc(qscale, sshift ? nblocks : 0);
+  const rsrc_t sr = make_rsrc(smax, scale_words(nblocks, sshift) * 4);
+  const uint32_t q2o = q2_or(sshift);
   const rsrc_t xr = make_rsrc(x, (int64_t)T * d_in * 2);
 
   // Item (row tile k, segment s): lane (li, g) takes block g of the segment in
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
     // kQ4 (blocks per row a multiple of 4): the word of blocks kb - g .. kb - g + 3
     // lies in the row, so inside the tensor
     st.q2 = kQ4 ? bld32(qr, ok ? (blk & ~3u) : kOOB) : bld8(qr, ok ? blk : kOOB);
-    st.S = __uint_as_float(bld32(sr, ok ? (blk >> 8) * 4u : kOOB));
+    st.S = __uint_as_float(bld32(sr, ok ? (blk >> sshift) * 4u : kOOB));
   };
   auto load_x = [&](int s, GemvX &st) {
     const int kb = 4 * (wv + kW * s) + g;
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int s, const GemvCodes &cs, const GemvX &xs2) {
-    const Nf4Planes t = make_planes(restore_scale(kQ4 ? (cs.q2 >> (8 * g)) & 0xffu : cs.q2, cs.S));
+    const Nf4Planes t = make_planes(restore_scale((kQ4 ? (cs.q2 >> (8 * g)) & 0xffu : cs.q2) | q2o, cs.S));
     // LDS path: token rows >= T only feed accumulator rows that are never stored,
     // and a block past the row end has an all-zero restore table, so both read
     // clamped, staged x without masking
@@ -467,6 +469,9 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
   const size_t xbytes = (size_t)T * (d_in + kXPad) * 2;
   const int di = (int)d_in, dn = (int)d_out, Tt = (int)T;
   const bool q4 = (d_in / kBlock) % 4 == 0;
+  // absmax-only storage: no scale codes (the kernel's q2 range is then empty)
+  const int sshift = qscale ? kDqShift : 0;
+  const uint8_t *qs = qscale ? qscale : codes;
   if (xbytes <= (size_t)kXLdsBytes) {
     if (dev >= 0 && !g_gemv_attr[dev]) {
       for (const void *f : {reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, true>),
@@ -478,16 +483,16 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
     }
     if (q4)
       k_gemv_fwd<kGvW, true, true><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
-          codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+          codes, qs, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync, sshift);
     else
       k_gemv_fwd<kGvW, true, false><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
-          codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+          codes, qs, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync, sshift);
   } else if (q4) {
     k_gemv_fwd<kGvW, false, true><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
-        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+        codes, qs, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync, sshift);
   } else {
     k_gemv_fwd<kGvW, false, false><<<dim3((unsigned)G), dim3(64 * kGvW), 0, st>>>(
-        codes, qscale, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync);
+        codes, qs, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync, sshift);
   }
   return hipGetLastError();
 }

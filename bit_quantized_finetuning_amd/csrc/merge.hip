@@ -43,7 +43,7 @@ constexpr size_t kMgLds = kMgALds + (size_t)kMgRows * kMgDPitch * 4;
 __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ qscale,
                                                const float *__restrict__ smax, int64_t d_out, int64_t d_in,
                                                const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int r,
-                                               float scale, uint16_t *__restrict__ out) {
+                                               float scale, uint16_t *__restrict__ out, int sshift) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mg_lds[];
   uint16_t *a_l = reinterpret_cast<uint16_t *>(mg_lds);
   float *d_l = reinterpret_cast<float *>(mg_lds + kMgALds);
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
       const bool ev = row < rows && k0 + c < d_in;
       const int64_t e = ev ? (n0 + row) * d_in + k0 + c : 0;  // a multiple of 8
       L.cw[k] = ev ? *reinterpret_cast<const uint32_t *>(codes + e / 2) : 0u;
-      L.q2[k] = ev ? qscale[e / kBlock] : 0u;
-      L.S[k] = ev ? smax[e / kBlock / kGroup] : 0.f;
+      L.q2[k] = ev ? (sshift ? (uint32_t)qscale[e / kBlock] : q2_or(0)) : 0u;
+      L.S[k] = ev ? smax[(e / kBlock) >> sshift] : 0.f;
     }
   };
 
@@ -196,7 +196,8 @@ hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float
   }
   const int64_t rows_per_wg = (int64_t)kMgRows * kMgTiles;
   const dim3 grid((unsigned)((d_in + kMgCols - 1) / kMgCols), (unsigned)((d_out + rows_per_wg - 1) / rows_per_wg));
-  k_merge<<<grid, dim3(256), kMgLds, st>>>(codes, qscale, smax, d_out, d_in, A, B, r, scale, out);
+  k_merge<<<grid, dim3(256), kMgLds, st>>>(codes, qscale, smax, d_out, d_in, A, B, r, scale, out,
+                                           qscale ? kDqShift : 0);
   return hipGetLastError();
 }
 

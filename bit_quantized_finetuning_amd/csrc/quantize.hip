@@ -14,7 +14,8 @@
 // 32-bit word. All eight passes' loads are issued before any arithmetic. The
 // block scales wait in LDS for the group maximum, then one thread per block
 // writes its 8-bit scale code. The kernel streams 4 (or 2) bytes in and ~0.52
-// bytes out per weight.
+// bytes out per weight. For absmax-only storage (sshift 0) each block's float32
+// absmax is written as its scale instead, and there is no group step.
 #include "kernels.h"
 
 namespace qlora {
@@ -23,7 +24,7 @@ template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, int64_t nblocks,
                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ qscale,
                                                   float *__restrict__ smax, uint32_t *__restrict__ flags,
-                                                  Nf4Consts c) {
+                                                  int sshift, Nf4Consts c) {
   constexpr int esz = kBf16In ? 2 : 4;
   constexpr int kPasses = kGroup / 32;
   __shared__ float s_blk[kGroup];
@@ -87,6 +88,11 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   __syncthreads();
 
   const float s = tid < nb ? s_blk[tid] : 0.f;
+  if (sshift == 0) {  // absmax-only storage: the block scales as they are
+    if (tid < nb) smax[b0 + tid] = s;
+    if (bad && flags) atomicOr(flags, 1u);
+    return;
+  }
   float S = s;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) S = fmaxf(S, __shfl_xor(S, off));
@@ -114,7 +120,7 @@ template <bool kBf16Out>
 __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__ codes,
                                                     const uint8_t *__restrict__ qscale,
                                                     const float *__restrict__ smax, int64_t n8,
-                                                    void *__restrict__ out, Nf4Consts c) {
+                                                    void *__restrict__ out, int sshift, Nf4Consts c) {
   __shared__ float cb[16];
   if (threadIdx.x == 0) {
 #pragma unroll
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
     const uint32_t cw = codes[i];
     const int64_t blk = i >> 3;
-    const float sh = restore_scale(qscale[blk], smax[blk >> 8]);
+    const float sh = sshift ? restore_scale(qscale[blk], smax[blk >> kDqShift]) : smax[blk];
     if (kBf16Out) {
       const Nf4Planes t = make_planes(sh);
       st16(static_cast<uint16_t *>(out) + i * 8, expand8(t, cw));
@@ -148,10 +154,13 @@ hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d
                            hipStream_t st) {
   const int64_t nblocks = d_out * d_in / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  const int sshift = qscale ? kDqShift : 0;
   if (bf16_in)
-    k_quantize<true><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, c);
+    k_quantize<true><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift,
+                                                                    c);
   else
-    k_quantize<false><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, c);
+    k_quantize<false><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift,
+                                                                     c);
   return hipGetLastError();
 }
 
@@ -161,10 +170,11 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const 
   int64_t grid = (n8 + 255) / 256;
   if (grid > 65536) grid = 65536;
   const uint32_t *cw = reinterpret_cast<const uint32_t *>(codes);
+  const int sshift = qscale ? kDqShift : 0;
   if (bf16_out)
-    k_dequantize<true><<<dim3((unsigned)grid), dim3(256), 0, st>>>(cw, qscale, smax, n8, out, c);
+    k_dequantize<true><<<dim3((unsigned)grid), dim3(256), 0, st>>>(cw, qscale, smax, n8, out, sshift, c);
   else
-    k_dequantize<false><<<dim3((unsigned)grid), dim3(256), 0, st>>>(cw, qscale, smax, n8, out, c);
+    k_dequantize<false><<<dim3((unsigned)grid), dim3(256), 0, st>>>(cw, qscale, smax, n8, out, sshift, c);
   return hipGetLastError();
 }
 

@@ -55,12 +55,13 @@ class QLoRALinear(torch.nn.Module):
     """
 
     def __init__(self, weight: torch.Tensor, r: int = 8, alpha: float = 16.0, freeze_A: bool = False,
-                 generator: torch.Generator | None = None):
+                 generator: torch.Generator | None = None, double_quant: bool = True):
         super().__init__()
         if weight.dim() != 2:
             raise ValueError("weight must be [d_out, d_in]")
         d_out, d_in = weight.shape
-        self.w = q.qlora_quantize(weight.contiguous())
+        # double_quant=False keeps the float32 absmax of every block (4.5 bits per weight)
+        self.w = q.qlora_quantize(weight.contiguous(), double_quant=double_quant)
         # the quantized buffers are frozen state, not parameters
         self.register_buffer("codes", self.w.codes, persistent=True)
         self.register_buffer("qscale", self.w.qscale, persistent=True)

@@ -7,7 +7,7 @@ there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
     qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_backward,
-    qlora_adamw_step, qlora_storage_bytes, qlora_workspace_bytes, qlora_nf4_codebook,
+    qlora_adamw_step, qlora_storage_bytes, qlora_storage_bytes_absmax, qlora_workspace_bytes, qlora_nf4_codebook,
     qlora_nf4_thresholds, qlora_status_string
 """
 
@@ -60,6 +60,8 @@ _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _
 _lib.qlora_backward.restype = ctypes.c_int
 _lib.qlora_storage_bytes.argtypes = [_i64, _i64]
 _lib.qlora_storage_bytes.restype = _sz
+_lib.qlora_storage_bytes_absmax.argtypes = [_i64, _i64]
+_lib.qlora_storage_bytes_absmax.restype = _sz
 _lib.qlora_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 _lib.qlora_workspace_bytes.restype = _sz
 _lib.qlora_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -111,6 +113,10 @@ def qlora_storage_bytes(d_out: int, d_in: int) -> int:
     return int(_lib.qlora_storage_bytes(d_out, d_in))
 
 
+def qlora_storage_bytes_absmax(d_out: int, d_in: int) -> int:
+    return int(_lib.qlora_storage_bytes_absmax(d_out, d_in))
+
+
 def qlora_workspace_bytes(d_out: int, d_in: int, T: int, r: int) -> int:
     return int(_lib.qlora_workspace_bytes(d_out, d_in, T, r))
 
@@ -125,27 +131,35 @@ def qlora_status_string(status: int) -> str:
 
 @dataclass
 class NF4Weight:
-    """A quantized frozen weight: the three buffers of qlora_nf4_weight plus its shape."""
+    """A quantized frozen weight: the three buffers of qlora_nf4_weight plus its shape.
+
+    qscale None is the absmax-only storage (4.5 bits per weight): smax then holds the float32 absmax of
+    every 64-weight block instead of one maximum per group of 256 blocks.
+    """
     d_out: int
     d_in: int
-    codes: torch.Tensor    # uint8 [d_out*d_in/2]
-    qscale: torch.Tensor   # uint8 [d_out*d_in/64]
-    smax: torch.Tensor     # float32 [ceil(d_out*d_in/64/256)]
+    codes: torch.Tensor           # uint8 [d_out*d_in/2]
+    qscale: torch.Tensor | None   # uint8 [d_out*d_in/64], or None
+    smax: torch.Tensor            # float32 [ceil(d_out*d_in/64/256)], or [d_out*d_in/64] without qscale
+
+    @property
+    def double_quant(self) -> bool:
+        return self.qscale is not None
 
     def _c(self):
-        return _Nf4Weight(self.d_out, self.d_in, self.codes.data_ptr(), self.qscale.data_ptr(),
-                          self.smax.data_ptr())
+        return _Nf4Weight(self.d_out, self.d_in, self.codes.data_ptr(),
+                          None if self.qscale is None else self.qscale.data_ptr(), self.smax.data_ptr())
 
     @staticmethod
-    def empty(d_out: int, d_in: int, device) -> "NF4Weight":
+    def empty(d_out: int, d_in: int, device, double_quant: bool = True) -> "NF4Weight":
         n = d_out * d_in
         nb = n // BLOCK
         ng = (nb + GROUP - 1) // GROUP
         # 16-byte aligned allocations (torch's caching allocator aligns to >= 512 bytes)
         return NF4Weight(d_out, d_in,
                          torch.empty(n // 2, dtype=torch.uint8, device=device),
-                         torch.empty(nb, dtype=torch.uint8, device=device),
-                         torch.empty(ng, dtype=torch.float32, device=device))
+                         torch.empty(nb, dtype=torch.uint8, device=device) if double_quant else None,
+                         torch.empty(ng if double_quant else nb, dtype=torch.float32, device=device))
 
 
 _workspaces: dict = {}
@@ -174,7 +188,9 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.Tensor | None = None) -> NF4Weight:
+def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.Tensor | None = None,
+                   double_quant: bool = True) -> NF4Weight:
+    """NF4-quantize W; double_quant=False keeps each block's float32 absmax (ignored when `out` is given)."""
     if W.dim() != 2 or not W.is_contiguous():
         raise ValueError("W must be a contiguous 2-D tensor")
     if W.dtype == torch.float32:
@@ -185,7 +201,7 @@ def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.T
         raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
     d_out, d_in = W.shape
     if out is None:
-        out = NF4Weight.empty(d_out, d_in, W.device)
+        out = NF4Weight.empty(d_out, d_in, W.device, double_quant)
     cw = out._c()
     _check(_lib.qlora_quantize(_ptr(W), dt, ctypes.byref(cw), _ptr(flags), _stream(W.device)), "qlora_quantize")
     return out

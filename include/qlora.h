@@ -75,6 +75,13 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
  *   smax   [ngroups]  f32  per-group maximum S_g of the block scales
  * Restored weight: w_hat = bf16( c[q] * (q2/256 * S_g) ), each product rounded
  * to float32 first (reconstruction equation of the "메모리 회계" section).
+ *
+ * Absmax-only storage (4.5 bits per weight: the same page and section, NF4
+ * paragraph, before double quantization) is selected by qscale == NULL:
+ *   smax   [nblocks]  f32  the block absmax s_k itself
+ * and w_hat = bf16( c[q] * s_k ). The codes are the same as with double
+ * quantization. Every entry point that takes a weight accepts either storage;
+ * absmax-only storage needs nblocks * 4 < 2^31 bytes of scales (else SHAPE).
  */
 typedef struct {
   int64_t d_out;
@@ -94,7 +101,8 @@ typedef struct {
  * Per block: s = max|w|; each w/s (IEEE float32 divide) takes the index of the
  * nearest NF4 level, ties to the lower index; s = 0 gives index 7 (exact zero).
  * Per group: S = max s; q2 = min(255, rint(fl32(s/S)*256)); S = 0 gives q2 = 0.
- * Bit-exact with the CPU oracle.
+ * With out->qscale == NULL (absmax-only storage) s itself goes to smax[block]
+ * and there is no group step. Bit-exact with the CPU oracle.
  */
 int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint32_t *flags,
                    hipStream_t stream);
@@ -195,6 +203,9 @@ int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, con
 
 /* Bytes of the quantized weight: n/2 + n/64 + 4*ceil(n/16384). */
 size_t qlora_storage_bytes(int64_t d_out, int64_t d_in);
+
+/* Bytes of the absmax-only storage (qscale == NULL): n/2 + 4*n/64, 4.5 bits per weight. */
+size_t qlora_storage_bytes_absmax(int64_t d_out, int64_t d_in);
 
 /* Workspace bytes sufficient for both qlora_forward and qlora_backward at these sizes. */
 size_t qlora_workspace_bytes(int64_t d_out, int64_t d_in, int64_t T, int32_t r);

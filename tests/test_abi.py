@@ -153,3 +153,21 @@ def test_adamw_rejects_bad_arguments():
     assert call(hp=q.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0.0)) == ERR_VALUE
     assert call(m=BAD) == ERR_ALIGN and call(param=BAD) == ERR_ALIGN
     assert call(n=0) == 0                                                          # nothing to do
+
+
+@pytest.mark.parametrize("shape", [(16, 64), (80, 320), (4096, 4096), (11008, 4096)])
+def test_absmax_storage_bytes_matches_oracle(shape):
+    assert q.qlora_storage_bytes_absmax(*shape) == oracle.storage_bytes_absmax(*shape)
+
+
+def test_absmax_weight_validation():
+    """qscale = NULL selects absmax-only storage: accepted as a weight, but its other checks still apply."""
+    absmax = _w(qs=None)
+    assert _fwd(absmax, x=None) == ERR_NULL          # the weight itself passes; the missing x is reported
+    assert _fwd(_w(qs=None, sm=None)) == ERR_NULL
+    assert _fwd(_w(qs=None, sm=BAD)) == ERR_ALIGN
+    assert _fwd(_w(qs=None, d_in=100)) == ERR_SHAPE
+    # one buffer range of float32 block scales: nblocks * 4 must stay below 2^31 bytes
+    assert _fwd(_w(d_out=1 << 20, d_in=1 << 15, qs=None)) == ERR_SHAPE
+    assert _fwd(_w(d_out=1 << 20, d_in=1 << 15, qs=GOOD), x=None) == ERR_NULL   # double quant: no such limit
+    assert q.lib.qlora_dequantize(ctypes.byref(_w(qs=None)), 1, None, None) == ERR_NULL
