@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true", help="skip the per-call-shape timings (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--storage", default="dq", choices=["dq", "absmax"],
+                   help="weight storage: NF4 with double-quantized scales (4.13 bits) or float32 block absmax (4.5)")
     p.add_argument("--paging", default="zerocopy", choices=["zerocopy", "dma"],
                    help="13b_paged_adamw: update m, v in host memory in place, or copy each page to the device and back")
     p.add_argument("--copy-calibration", action="store_true",
@@ -75,9 +77,14 @@ def parse():
     return p.parse_args()
 
 
+ABSMAX_STORAGE = [False]  # set from --storage
+
+
 def weight_bytes(d_out, d_in):
     n = d_out * d_in
     nb = n // 64
+    if ABSMAX_STORAGE[0]:
+        return n // 2 + 4 * nb               # codes + one float32 scale per block (4.5 bits)
     return n // 2 + nb + 4 * ((nb + 255) // 256)
 
 
@@ -115,6 +122,9 @@ def main():
     from bit_quantized_finetuning_amd import synth
 
     dev = torch.device("cuda:0")
+    ABSMAX_STORAGE[0] = args.storage == "absmax"
+    if ABSMAX_STORAGE[0] and args.workload in ("merge_llama7b", "14b_quantize", "13b_paged_adamw"):
+        sys.exit(f"--storage absmax is measured on the forward/backward workloads, not {args.workload}")
     if args.workload == "merge_llama7b":
         return bench_merge(args, torch, q, synth, dev)
     if args.workload == "14b_quantize":
@@ -134,7 +144,7 @@ def main():
     projs = []
     for pi, p in enumerate(wl.projections):
         W = torch.from_numpy(synth.weight(seed_cfg, pi, p.d_out, p.d_in, wl.weight_dtype)).to(dev)
-        w0 = q.qlora_quantize(W)
+        w0 = q.qlora_quantize(W, double_quant=not ABSMAX_STORAGE[0])
         del W
         A0 = B0 = None
         if p.r > 0:
@@ -143,7 +153,8 @@ def main():
         ncopy = chunk * nT if not bw else 2
         copies = [(w0, A0, B0)]
         for _ in range(ncopy - 1):
-            copies.append((q.NF4Weight(p.d_out, p.d_in, w0.codes.clone(), w0.qscale.clone(), w0.smax.clone()),
+            copies.append((q.NF4Weight(p.d_out, p.d_in, w0.codes.clone(),
+                                       None if w0.qscale is None else w0.qscale.clone(), w0.smax.clone()),
                            None if A0 is None else A0.clone(), None if B0 is None else B0.clone()))
         xs = {T: dev16(synth.tokens(seed_cfg, pi, T, p.d_in)[1]) for T in wl.tokens}
         dys = {T: dev16(synth.upstream_grad(seed_cfg, pi, T, p.d_out)[1]) for T in wl.tokens} if bw else {}
@@ -348,6 +359,8 @@ def main():
         "config": {"workload": wl.description, "projections": [f"{p.d_out}x{p.d_in}" for p in wl.projections],
                    "tokens": list(wl.tokens), "lora_r": wl.projections[0].r, "lora_alpha": wl.projections[0].alpha,
                    "backward": bw, "graph_steps": chunk if graphs else 0,
+                   "weight_storage": ("NF4 + float32 absmax per 64-weight block (4.5 bits)" if ABSMAX_STORAGE[0]
+                                      else "NF4 + double-quantized block scales (4.127 bits)"),
                    "weight_copies_per_projection": len(projs[0][1]),
                    **({"layers_in_stack": wl.layers, "layers_per_step": 1} if wl.layers > 1 else {})},
         "tflops": round(tflops, 3),
@@ -427,7 +440,11 @@ def cpu_baseline(args, wl, seed_cfg, wbytes_step):
     prepared = []
     for pi, p in enumerate(wl.projections):
         W = synth.weight(seed_cfg, pi, p.d_out, p.d_in, wl.weight_dtype)
-        codes, q2, S = oracle.quantize(W)
+        if ABSMAX_STORAGE[0]:
+            codes, S = oracle.quantize_absmax(W)
+            q2 = None
+        else:
+            codes, q2, S = oracle.quantize(W)
         (A, _), (B, _) = synth.adapters(seed_cfg, pi, p.d_out, p.d_in, p.r)
         xs = {T: synth.tokens(seed_cfg, pi, T, p.d_in)[0] for T in wl.tokens}
         prepared.append((p, codes, q2, S, A, B, xs))
@@ -435,7 +452,10 @@ def cpu_baseline(args, wl, seed_cfg, wbytes_step):
     t_start = time.perf_counter()
     while True:
         for p, codes, q2, S, A, B, xs in prepared:
-            _, wb = oracle.dequantize(codes, q2, S, p.d_out, p.d_in)
+            if q2 is None:
+                _, wb = oracle.dequantize_absmax(codes, S, p.d_out, p.d_in)
+            else:
+                _, wb = oracle.dequantize(codes, q2, S, p.d_out, p.d_in)
             for T in wl.tokens:
                 oracle.lora_forward(wb, xs[T], A, B, p.alpha, p.r)
         done_steps += 1
