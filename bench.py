@@ -26,15 +26,20 @@ Other workloads are records, not the headline line:
   13b_4096tok / 65b_layer / linear1024 / 14b_stack  the MFMA GEMM regime
       (forward + backward; 14b_stack: one of the 40 identical layers of the
       14B-style stack, bf16 source weights, 2048 tokens, LoRA r=8 on q and v);
+  14b_stack_fused  the same layer with q/k/v and gate/up each stacked into one
+      call that reads its input once (q and v adapters as one block-diagonal
+      rank-16 pair);
   14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack
       (13.2 G parameters, generated on the device from a seeded generator);
   merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two
       LLaMA-7B projections with r = 64;
   13b_paged_adamw  the 13b_4096tok step, timed without and with an AdamW update
-      of every A and B whose state (float32 master, m, v) sits in pinned host
-      memory; the update of a projection runs on a side stream beside the next
-      projection's forward and backward. Reported: the step with the update and
-      the throughput lost to it.
+      of every A and B whose moments m, v sit in pinned host memory (float32
+      master on the device); the update of a projection runs on a side stream
+      beside the next projection's forward and backward. Reported: the step with
+      the update and the throughput lost to it.
+  --storage absmax  any forward/backward workload on absmax-only weights (one
+      float32 scale per 64-weight block, 4.5 bits) instead of double quant.
 """
 
 from __future__ import annotations
@@ -53,7 +58,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_quantize",
+WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused",
+                    "14b_quantize",
                     "merge_llama7b", "13b_paged_adamw"]
 
 
@@ -150,6 +156,12 @@ def main():
         if p.r > 0:
             (_, A_bits), (_, B_bits) = synth.adapters(seed_cfg, pi, p.d_out, p.d_in, p.r)
             A0, B0 = dev16(A_bits), dev16(B_bits)
+            if p.b_rows:  # stacked projections: block-diagonal B (adapter k on its projection's rows only)
+                mask = torch.zeros_like(B0, dtype=torch.bool)
+                rk = p.r // len(p.b_rows)
+                for k, (r0, r1) in enumerate(p.b_rows):
+                    mask[r0:r1, k * rk:(k + 1) * rk] = True
+                B0 = torch.where(mask, B0, torch.zeros_like(B0))
         ncopy = chunk * nT if not bw else 2
         copies = [(w0, A0, B0)]
         for _ in range(ncopy - 1):

@@ -84,3 +84,75 @@ class QLoRALinear(torch.nn.Module):
     def merged_weight(self) -> torch.Tensor:
         """bf16 [d_out, d_in] = bf16(W_hat + (alpha/r) B A), for export."""
         return q.qlora_merge(self.w, self.A, self.B, self.alpha)
+
+
+class QLoRAFusedLinear(torch.nn.Module):
+    """Several projections of one input (q/k/v, or gate/up) as one quantized weight and one call.
+
+    The weights are stacked along d_out and quantized as one matrix, so every forward reads x once and streams all
+    of them in one launch, and the backward's dX is the sum over the projections in one contraction. With the
+    pages' placement of adapters on some projections only ("무엇을 돌렸나" on the GPU-fit page: LoRA on q and v),
+    each adapted projection i has its own A_i [r, d_in] and B_i [d_out_i, r]. The call uses their stack
+    A = [A_1; A_2; ...] and the block-diagonal B that puts B_i on projection i's rows and adapter i's columns,
+    with alpha scaled by the number of adapters so that the scale stays alpha / r: every output row then gets
+    exactly its own projection's term (the zero entries add exact zeros), and autograd returns dA_i, dB_i from
+    the stacked gradients.
+
+    The stacked quantization equals quantizing each projection alone whenever each projection's block count is a
+    multiple of the 256-block group (true for the usual shapes: d_out_i * d_in / 64 % 256 == 0), and always with
+    absmax-only storage.
+    """
+
+    def __init__(self, weights, r: int = 8, alpha: float = 16.0, adapted=None, double_quant: bool = True,
+                 generator: torch.Generator | None = None):
+        super().__init__()
+        weights = [w.contiguous() for w in weights]
+        d_in = weights[0].shape[1]
+        if any(w.dim() != 2 or w.shape[1] != d_in for w in weights):
+            raise ValueError("all weights must be [d_out_i, d_in] with one d_in")
+        self.d_outs = [int(w.shape[0]) for w in weights]
+        self.d_in, self.r, self.alpha = d_in, r, float(alpha)
+        self.adapted = list(adapted) if adapted is not None else [True] * len(weights)
+        if len(self.adapted) != len(weights):
+            raise ValueError("one adapted flag per weight")
+        n_ad = sum(self.adapted) if r > 0 else 0
+        if n_ad * r > q.MAX_RANK:
+            raise ValueError(f"{n_ad} adapters of rank {r} exceed the library's rank limit {q.MAX_RANK}")
+        self.w = q.qlora_quantize(torch.cat(weights, 0), double_quant=double_quant)
+        self.register_buffer("codes", self.w.codes, persistent=True)
+        self.register_buffer("qscale", self.w.qscale, persistent=True)
+        self.register_buffer("smax", self.w.smax, persistent=True)
+        self.A = torch.nn.ParameterList()
+        self.B = torch.nn.ParameterList()
+        dev = weights[0].device
+        for d_out, ad in zip(self.d_outs, self.adapted):
+            if ad and r > 0:
+                A = torch.randn(r, d_in, device=dev, generator=generator) * 0.02
+                self.A.append(torch.nn.Parameter(A.to(torch.bfloat16)))
+                self.B.append(torch.nn.Parameter(torch.zeros(d_out, r, dtype=torch.bfloat16, device=dev)))
+
+    def stacked_adapter(self):
+        """(A [n r, d_in], block-diagonal B [sum d_out_i, n r]) built from the parameters (differentiable)."""
+        if len(self.A) == 0:
+            return None, None
+        A = torch.cat(list(self.A), 0)
+        cols = len(self.A) * self.r
+        parts, k = [], 0
+        for d_out, ad in zip(self.d_outs, self.adapted):
+            if ad and self.r > 0:
+                B = self.B[k]
+                parts.append(torch.nn.functional.pad(B, (k * self.r, cols - (k + 1) * self.r)))
+                k += 1
+            else:
+                parts.append(torch.zeros(d_out, cols, dtype=torch.bfloat16, device=A.device))
+        return A, torch.cat(parts, 0)
+
+    def forward(self, x: torch.Tensor):
+        """Returns one output per projection, [..., d_out_i] each (views of the single call's output)."""
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.d_in).to(torch.bfloat16).contiguous()
+        A, B = self.stacked_adapter()
+        n_ad = len(self.A)
+        alpha = self.alpha * n_ad if n_ad else self.alpha  # scale alpha / (n_ad r) = self.alpha / r
+        h = QLoRALinearFunction.apply(x2, A, B, self.w, alpha)
+        return tuple(t.reshape(*lead, t.shape[-1]) for t in torch.split(h, self.d_outs, dim=1))

@@ -31,6 +31,10 @@ class Projection:
     d_in: int
     r: int           # LoRA rank, 0 = frozen projection without adapter
     alpha: float
+    # Stacked projections (one call for several projections of one input): the row range of each adapted
+    # projection; adapter k then owns B's rows in b_rows[k] and columns k r/len(b_rows) .. (k+1) r/len(b_rows),
+    # and B is zero elsewhere. Empty: one projection, B dense.
+    b_rows: tuple = ()
 
 
 @dataclass(frozen=True)
@@ -64,6 +68,14 @@ WORKLOADS = {
                     Projection("gate_proj", 22016, 8192, 64, 16.0),
                     Projection("up_proj", 22016, 8192, 64, 16.0),
                     Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
+    # The same layer with the projections of one input stacked into one call each: q/k/v (7168 x 5120, the
+    # q and v adapters as a rank-16 block-diagonal pair, alpha doubled so the scale stays 16/8) and gate/up.
+    "14b_stack_fused": Workload("14b_stack_fused", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 "
+                   "alpha=16 on q/v, 2048 tokens, fwd+bwd, q/k/v and gate/up each as one stacked call",
+                   (Projection("qkv_proj", 7168, 5120, 16, 32.0, b_rows=((0, 5120), (6144, 7168))),
+                    Projection("o_proj", 5120, 5120, 0, 16.0),
+                    Projection("gate_up_proj", 34816, 5120, 0, 16.0),
+                    Projection("down_proj", 5120, 17408, 0, 16.0)), (2048,), True, "bf16", layers=40),
     # 14B-style stack: k/v are 1024x5120 (8 KV heads x 128); LoRA r=8 on q and v only.
     "14b_stack": Workload("14b_stack", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 alpha=16 "
                    "on q/v, 2048 tokens, fwd+bwd",
@@ -76,7 +88,8 @@ WORKLOADS = {
                     Projection("down_proj", 5120, 17408, 0, 16.0)), (2048,), True, "bf16", layers=40),
 }
 # second component of every RNG seed list, one per workload
-WORKLOAD_SEED = {"linear1024": 1, "llama7b_skinny": 2, "13b_4096tok": 3, "65b_layer": 4, "14b_stack": 5}
+WORKLOAD_SEED = {"linear1024": 1, "llama7b_skinny": 2, "13b_4096tok": 3, "65b_layer": 4, "14b_stack": 5,
+                 "14b_stack_fused": 6}
 
 
 def rng(config: int, projection: int, tensor: int, seed: int = 0) -> np.random.Generator:

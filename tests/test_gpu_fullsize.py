@@ -155,3 +155,11 @@ def test_merge_llama7b_full():
     torch.cuda.synchronize()
     assert_within_one_bf16_ulp("merged", out, oracle.lora_merge(wb, A, B, alpha, r),
                                merge_float32_slack(wb, A, B, alpha, r))
+
+
+@pytest.mark.parametrize("d_out,d_in,r,alpha,pi", [(7168, 5120, 16, 32.0, 0), (34816, 5120, 0, 16.0, 2)])
+def test_14b_stack_fused_calls_2048_tokens(d_out, d_in, r, alpha, pi):
+    """The stacked calls of the 14B-style layer at full size: q/k/v as one 7168x5120 weight with a rank-16
+    adapter (alpha 32), gate/up as one 34816x5120 weight."""
+    say(f"14B stack fused {d_out}x{d_in} r={r} T=2048")
+    _sampled_fwd_bwd(d_out, d_in, r, 2048, synth.WORKLOAD_SEED["14b_stack_fused"], pi, wdtype="bf16", alpha=alpha)

@@ -203,3 +203,20 @@ def test_bf16_round_f64_agrees_with_float32_route_on_float32_values():
     for a in (v, ties, -ties, nties, -nties):
         ref = oracle.bf16_round(a).astype(np.float64)
         assert np.array_equal(oracle.bf16_round_f64(a.astype(np.float64)), ref)
+
+
+def test_fused_stack_workload_is_the_same_layer():
+    """The stacked-call variant of the 14B-style layer holds the same weights and trainable parameters: q/k/v
+    stacked to 7168 rows and gate/up to 34816, the q and v adapters as a block-diagonal rank-16 pair whose
+    scale alpha/r is unchanged."""
+    sep = synth.WORKLOADS["14b_stack"]
+    fus = synth.WORKLOADS["14b_stack_fused"]
+    assert sum(p.d_out * p.d_in for p in sep.projections) == sum(p.d_out * p.d_in for p in fus.projections)
+    qkv = fus.projections[0]
+    q_, k_, v_ = sep.projections[:3]
+    assert qkv.d_out == q_.d_out + k_.d_out + v_.d_out
+    assert qkv.b_rows == ((0, q_.d_out), (q_.d_out + k_.d_out, qkv.d_out))
+    assert qkv.alpha / qkv.r == q_.alpha / q_.r == v_.alpha / v_.r
+    trainable = sum(r1 - r0 for r0, r1 in qkv.b_rows) * (qkv.r // 2) + qkv.r * qkv.d_in
+    assert trainable == sum(p.r * (p.d_in + p.d_out) for p in sep.projections)
+    assert fus.projections[2].d_out == sep.projections[4].d_out + sep.projections[5].d_out
