@@ -14,7 +14,16 @@
 // 32-bit word. All eight passes' loads are issued before any arithmetic. The
 // block scales wait in LDS for the group maximum, then one thread per block
 // writes its 8-bit scale code. The kernel streams 4 (or 2) bytes in and ~0.52
-// bytes out per weight. For absmax-only storage (sshift 0) each block's float32
+// bytes out per weight.
+//
+// Nearest level: the index is the number of the 15 float32 thresholds at or
+// below x = w/s (x is in [-1, 1]). Instead of 15 comparisons per weight, x's
+// float32 bits pick one of 64 buckets: sign, binade (2^-5 .. 1 in six steps,
+// everything smaller in one) and the top two significand bits. No bucket
+// holds more than one threshold, so the count is the bucket's base count
+// plus one comparison with its threshold (+inf where it has none). The
+// buckets are built per workgroup from the thresholds; checked against the
+// plain count for every float32 in [-1, 1]. For absmax-only storage (sshift 0) each block's float32
 // absmax is written as its scale instead, and there is no group step.
 #include "kernels.h"
 
@@ -29,6 +38,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   constexpr int kPasses = kGroup / 32;
   __shared__ float s_blk[kGroup];
   __shared__ float s_red[4];
+  __shared__ float2 bucket[64];  // {threshold inside the bucket or +inf, count of thresholds below it}
   const int tid = threadIdx.x;
   const int64_t b0 = (int64_t)blockIdx.x * kGroup;
   const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
@@ -44,6 +54,36 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
     raw[p][0] = bld16(wr, off);
     if (!kBf16In) raw[p][kBf16In ? 0 : 1] = bld16(wr, off + 16);
   }
+
+  // Bucket b = sign * 32 + e * 4 + m covers magnitudes [lo, hi): e = 0 is
+  // [0, 2^-5); e = 1 .. 6 the binade [2^(e-6), 2^(e-5)) cut into quarters by m.
+  // A positive x in it has every threshold <= lo below it and can pass one in
+  // (lo, hi); a negative x (in (-hi, -lo]) has every threshold <= -hi below it
+  // and can pass one in (-hi, -lo].
+  if (tid < 64) {
+    const int sg = tid >> 5, e = (tid >> 2) & 7, m = tid & 3;
+    float lo = 0.f, hi = 0.03125f;
+    if (e > 0) {
+      const float b = __builtin_ldexpf(1.f, e - 6);
+      lo = b + 0.25f * b * (float)m;  // exact
+      hi = b + 0.25f * b * (float)(m + 1);
+    }
+    float cand = __builtin_inff();
+    int below = 0;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      const float t = c.thr[j];
+      if (sg == 0) {
+        below += t <= lo;
+        if (t > lo && t < hi) cand = t;
+      } else {
+        below += t <= -hi;
+        if (t > -hi && t <= -lo) cand = t;
+      }
+    }
+    bucket[tid] = make_float2(cand, (float)below);
+  }
+  __syncthreads();
 
   uint32_t bad = 0;
 #pragma unroll
@@ -75,9 +115,10 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = m > 0.f ? w[e] / m : 0.f;  // IEEE float32 divide
-      uint32_t q = 0;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) q += (x >= c.thr[j]) ? 1u : 0u;
+      const uint32_t xb = __float_as_uint(x);
+      const int be = min(max((int)((xb >> 23) & 0xffu) - 121, 0), 6);
+      const float2 bk = bucket[((xb >> 31) << 5) | ((uint32_t)be << 2) | ((xb >> 21) & 3u)];
+      const uint32_t q = (uint32_t)bk.y + (x >= bk.x ? 1u : 0u);
       word |= q << nibble_shift(e);
     }
     if (b < nb) {
