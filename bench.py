@@ -23,6 +23,8 @@ bytes per launch over its mean launch duration in the timed region; `cpu_baselin
 is the CPU oracle timed on a bounded sample of the same workload.
 
 Other workloads are records, not the headline line:
+  65b_skinny  the same weight-streaming forward (T = 1, 16; r = 64) on the 65B layer's
+      8192x8192, 22016x8192 and 8192x22016 weights (34-93 MB per call);
   13b_4096tok / 65b_layer / linear1024 / 14b_stack  the MFMA GEMM regime
       (forward + backward; 14b_stack: one of the 40 identical layers of the
       14B-style stack, bf16 source weights, 2048 tokens, LoRA r=8 on q and v);
@@ -58,7 +60,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-WORKLOAD_CHOICES = ["llama7b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused",
+WORKLOAD_CHOICES = ["llama7b_skinny", "65b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused",
                     "14b_quantize",
                     "merge_llama7b", "13b_paged_adamw"]
 

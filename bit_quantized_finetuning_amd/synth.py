@@ -68,6 +68,13 @@ WORKLOADS = {
                     Projection("gate_proj", 22016, 8192, 64, 16.0),
                     Projection("up_proj", 22016, 8192, 64, 16.0),
                     Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
+    # The weight-streaming regime on the 65B layer's larger weights (34-93 MB per call instead of 9-23 MB):
+    # how close the T <= 16 kernel gets to HBM once the stream is long against its fixed latency.
+    "65b_skinny": Workload("65b_skinny", "65B decoder-layer projections 8192x8192, 22016x8192 and 8192x22016, "
+                   "LoRA r=64 alpha=16, 1/16 tokens, forward",
+                   (Projection("q_proj", 8192, 8192, 64, 16.0),
+                    Projection("gate_proj", 22016, 8192, 64, 16.0),
+                    Projection("down_proj", 8192, 22016, 64, 16.0)), (1, 16), False, "f32"),
     # The same layer with the projections of one input stacked into one call each: q/k/v (7168 x 5120, the
     # q and v adapters as a rank-16 block-diagonal pair, alpha doubled so the scale stays 16/8) and gate/up.
     "14b_stack_fused": Workload("14b_stack_fused", "14B-style stack, hidden 5120, MLP 17408, 40 layers, LoRA r=8 "
@@ -89,7 +96,7 @@ WORKLOADS = {
 }
 # second component of every RNG seed list, one per workload
 WORKLOAD_SEED = {"linear1024": 1, "llama7b_skinny": 2, "13b_4096tok": 3, "65b_layer": 4, "14b_stack": 5,
-                 "14b_stack_fused": 6}
+                 "14b_stack_fused": 6, "65b_skinny": 7}
 
 
 def rng(config: int, projection: int, tensor: int, seed: int = 0) -> np.random.Generator:
