@@ -95,6 +95,8 @@ int validate_weight(const qlora_nf4_weight *W) {
   if (W->d_out < 1 || W->d_in < QLORA_BLOCK || W->d_in % QLORA_BLOCK != 0 || W->d_out % 16 != 0)
     return QLORA_ERR_SHAPE;
   if (W->d_out > kMaxDim || W->d_in > kMaxDim) return QLORA_ERR_SHAPE;
+  // block indices are 32-bit in the kernels
+  if (W->d_out * W->d_in / QLORA_BLOCK >= ((int64_t)1 << 32)) return QLORA_ERR_SHAPE;
   // absmax-only storage: the kernels address the float32 block scales as one buffer range
   if (!W->qscale && W->d_out * W->d_in / QLORA_BLOCK * 4 >= ((int64_t)1 << 31)) return QLORA_ERR_SHAPE;
   if (!aligned16(W->codes) || (W->qscale && !aligned16(W->qscale)) || !aligned16(W->smax)) return QLORA_ERR_ALIGN;

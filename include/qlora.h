@@ -22,7 +22,8 @@
  *   - Work is enqueued asynchronously on `stream` (0 = the legacy default stream).
  *   - Arguments are validated on the host before anything is enqueued. On any
  *     error the call returns a negative status and writes no output byte.
- *   - Shapes: d_in % 64 == 0, d_out % 16 == 0, both <= QLORA_MAX_DIM;
+ *   - Shapes: d_in % 64 == 0, d_out % 16 == 0, both <= QLORA_MAX_DIM, and
+ *     fewer than 2^32 blocks (d_out * d_in < 2^38);
  *     1 <= T <= QLORA_MAX_TOKENS; 0 <= r <= 256 with r % 8 == 0.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Calls that run concurrently (other streams or threads) must not share a

@@ -171,3 +171,9 @@ def test_absmax_weight_validation():
     assert _fwd(_w(d_out=1 << 20, d_in=1 << 15, qs=None)) == ERR_SHAPE
     assert _fwd(_w(d_out=1 << 20, d_in=1 << 15, qs=GOOD), x=None) == ERR_NULL   # double quant: no such limit
     assert q.lib.qlora_dequantize(ctypes.byref(_w(qs=None)), 1, None, None) == ERR_NULL
+
+
+def test_weight_with_2_pow_32_blocks_is_refused():
+    """Block indices are 32-bit in the kernels: d_out * d_in / 64 must stay below 2^32."""
+    assert _fwd(_w(d_out=1 << 20, d_in=1 << 18), x=None) == ERR_SHAPE
+    assert _fwd(_w(d_out=(1 << 20) - 16, d_in=1 << 18), x=None) == ERR_NULL   # just below: the weight passes
