@@ -163,3 +163,44 @@ def test_14b_stack_fused_calls_2048_tokens(d_out, d_in, r, alpha, pi):
     adapter (alpha 32), gate/up as one 34816x5120 weight."""
     say(f"14B stack fused {d_out}x{d_in} r={r} T=2048")
     _sampled_fwd_bwd(d_out, d_in, r, 2048, synth.WORKLOAD_SEED["14b_stack_fused"], pi, wdtype="bf16", alpha=alpha)
+
+
+def test_maximum_token_count():
+    """T = 2^24 (the ABI's maximum) on a 16 x 64 weight with r = 8: h and dX on 256 sampled token rows, u and v on
+    the same rows, and dA, dB in full (sums over all 2^24 tokens, which the oracle forms in float64 in chunks).
+    The inputs come from a seeded device generator: 2^24 x 64 numbers are too many to draw on the host."""
+    T, d_out, d_in, r, alpha = 1 << 24, 16, 64, 8, 16.0
+    say(f"maximum T = {T}")
+    cfg = synth.WORKLOAD_SEED["linear1024"]
+    W_np = synth.weight(cfg, 9, d_out, d_in)
+    w, wb = _quantize_full(W_np)
+    (A, A_bits), (B, B_bits) = synth.adapters(cfg, 9, d_out, d_in, r)
+    Ad, Bd = bits_to_bf16(A_bits), bits_to_bf16(B_bits)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    x = torch.randn(T, d_in, device="cuda", generator=gen).to(torch.bfloat16)
+    dY = torch.randn(T, d_out, device="cuda", generator=gen).to(torch.bfloat16)
+    h, u = q.qlora_forward(w, x, Ad, Bd, alpha, save_u=True)
+    dX, dA, dB = q.qlora_backward(w, x, dY, Ad, Bd, alpha, u_saved=u)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(T, 256, replace=False))
+    rows[-1] = T - 1  # the last token row too
+    ri = torch.from_numpy(rows).cuda()
+    xs = x[ri].double().cpu().numpy()
+    dYs = dY[ri].double().cpu().numpy()
+    h_ref, u_ref = oracle.lora_forward(wb, xs, A, B, alpha, r)
+    assert_close("h rows", h[ri], h_ref)
+    assert_close("u rows", u[ri], u_ref)
+    dX_ref, _, _ = oracle.lora_backward(wb, xs, dYs, A, B, alpha, r)
+    assert_close("dX rows", dX[ri], dX_ref)
+    # dA and dB are sums over the tokens: the oracle's values for chunks of 2^20 rows, added in float64
+    dA_ref = np.zeros((r, d_in))
+    dB_ref = np.zeros((d_out, r))
+    for c0 in range(0, T, 1 << 20):
+        xc = x[c0:c0 + (1 << 20)].double().cpu().numpy()
+        dYc = dY[c0:c0 + (1 << 20)].double().cpu().numpy()
+        _, dA_c, dB_c = oracle.lora_backward(wb, xc, dYc, A, B, alpha, r)
+        dA_ref += dA_c
+        dB_ref += dB_c
+    assert_close("dA (all tokens)", dA, dA_ref)
+    assert_close("dB (all tokens)", dB, dB_ref)
