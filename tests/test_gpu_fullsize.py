@@ -204,3 +204,29 @@ def test_maximum_token_count():
         dB_ref += dB_c
     assert_close("dA (all tokens)", dA, dA_ref)
     assert_close("dB (all tokens)", dB, dB_ref)
+
+
+@pytest.mark.parametrize("d_out,d_in,T", [(16, 1 << 20, 1), (16, 1 << 20, 100), (1 << 20, 64, 16), (1 << 20, 64, 100)])
+def test_maximum_dimensions(d_out, d_in, T):
+    """d_in or d_out at the ABI's maximum (2^20) with r = 8: the weight bit-exact, then h, u, dX, dA and dB in
+    full against the oracle (T = 1 and 16 take the weight-streaming forward, T = 100 the GEMMs)."""
+    r, alpha = 8, 16.0
+    cfg = synth.WORKLOAD_SEED["linear1024"]
+    say(f"maximum dims {d_out}x{d_in} T={T}")
+    W_np = synth.weight(cfg, 10, d_out, d_in)
+    w, wb = _quantize_full(W_np)
+    del W_np
+    (A, A_bits), (B, B_bits) = synth.adapters(cfg, 10, d_out, d_in, r)
+    x, x_bits = synth.tokens(cfg, 10, T, d_in)
+    dY, dY_bits = synth.upstream_grad(cfg, 10, T, d_out)
+    Ad, Bd = bits_to_bf16(A_bits), bits_to_bf16(B_bits)
+    h, u = q.qlora_forward(w, bits_to_bf16(x_bits), Ad, Bd, alpha, save_u=True)
+    dX, dA, dB = q.qlora_backward(w, bits_to_bf16(x_bits), bits_to_bf16(dY_bits), Ad, Bd, alpha, u_saved=u)
+    torch.cuda.synchronize()
+    h_ref, u_ref = oracle.lora_forward(wb, x, A, B, alpha, r)
+    assert_close("h", h, h_ref)
+    assert_close("u", u, u_ref)
+    dX_ref, dA_ref, dB_ref = oracle.lora_backward(wb, x, dY, A, B, alpha, r)
+    assert_close("dX", dX, dX_ref)
+    assert_close("dA", dA, dA_ref)
+    assert_close("dB", dB, dB_ref)
