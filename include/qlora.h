@@ -28,6 +28,9 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Calls that run concurrently (other streams or threads) must not share a
  *     workspace.
+ *   - The header is plain C: it needs only hip_runtime_api.h for hipStream_t.
+ *     A host compiler other than hipcc defines __HIP_PLATFORM_AMD__ for that
+ *     header, as `hipconfig --cpp_config` prints.
  */
 #ifndef QLORA_H
 #define QLORA_H

@@ -177,3 +177,29 @@ def test_weight_with_2_pow_32_blocks_is_refused():
     """Block indices are 32-bit in the kernels: d_out * d_in / 64 must stay below 2^32."""
     assert _fwd(_w(d_out=1 << 20, d_in=1 << 18), x=None) == ERR_SHAPE
     assert _fwd(_w(d_out=(1 << 20) - 16, d_in=1 << 18), x=None) == ERR_NULL   # just below: the weight passes
+
+
+def test_header_and_library_from_plain_c(tmp_path):
+    """A C11 program (gcc, not hipcc) includes include/qlora.h, links libqlora.so and calls the host-side entry
+    points: the codebook and thresholds equal the oracle's bit for bit, the sizes equal the oracle's formulas, and
+    a malformed weight is refused with QLORA_ERR_SHAPE."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    libdir = os.path.dirname(q.LIB_PATH)
+    exe = tmp_path / "abi_check"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "c_abi", "abi_check.c"), "-L", libdir, "-lqlora",
+                    "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    vals = np.array([float.fromhex(v) for v in out[:31]], dtype=np.float32)
+    assert np.array_equal(vals[:16].view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+    assert np.array_equal(vals[16:31].view(np.uint32), oracle.nf4_thresholds_f32().view(np.uint32))
+    sb, sa, ws = (int(v) for v in out[31].split())
+    assert sb == oracle.storage_bytes(4096, 4096) and sa == oracle.storage_bytes_absmax(4096, 4096)
+    assert ws == q.qlora_workspace_bytes(4096, 4096, 16, 64)
+    assert out[32].split()[0] == str(ERR_SHAPE)
