@@ -9,7 +9,8 @@ Places": gradients pass through the restored W to A and B). Every step runs in
 the HIP library through the C-ABI binding; this file only marshals tensors.
 
 The forward saves u = x A^T (T x r float32) for the backward's dB, so u is not
-recomputed. With a frozen A (LoRA-FA: "8GB, 12GB, 16GB, 24GB GPU에서 몇 B
+recomputed; with recompute_u the layer keeps only x and the backward forms u
+again (T x r float32 less memory per layer, one more pass over x). With a frozen A (LoRA-FA: "8GB, 12GB, 16GB, 24GB GPU에서 몇 B
 모델까지 LoRA 학습이 될까", section "LoRA 변형을 바꿔도 답이 같은 이유" -- the
 layer input is not kept) the input x is not saved either: dX needs only dY,
 and dB only u.
@@ -26,10 +27,11 @@ class QLoRALinearFunction(torch.autograd.Function):
     """x [T, d_in] bf16, A [r, d_in] bf16, B [d_out, r] bf16 -> h [T, d_out] bf16."""
 
     @staticmethod
-    def forward(ctx, x, A, B, w: q.NF4Weight, alpha: float):
+    def forward(ctx, x, A, B, w: q.NF4Weight, alpha: float, recompute_u: bool = False):
         r = 0 if A is None else A.shape[0]
-        h, u = q.qlora_forward(w, x, A, B, alpha, save_u=r > 0)
-        keep_x = A is not None and A.requires_grad
+        keep_u = r > 0 and not recompute_u
+        h, u = q.qlora_forward(w, x, A, B, alpha, save_u=keep_u)
+        keep_x = A is not None and (A.requires_grad or not keep_u)
         ctx.w, ctx.alpha, ctx.r = w, alpha, r
         ctx.save_for_backward(x if keep_x else None, A, B, u)
         return h
@@ -43,7 +45,7 @@ class QLoRALinearFunction(torch.autograd.Function):
         dX, dA, dB = q.qlora_backward(ctx.w, x, dh.contiguous(), A, B, ctx.alpha, u_saved=u, need_dx=need_dx,
                                       need_dA=need_dA, need_dB=need_dB)
         # dA, dB come back in float32 (the library's gradient precision); autograd wants the parameters' dtype
-        return (dX, None if dA is None else dA.to(A.dtype), None if dB is None else dB.to(B.dtype), None, None)
+        return (dX, None if dA is None else dA.to(A.dtype), None if dB is None else dB.to(B.dtype), None, None, None)
 
 
 class QLoRALinear(torch.nn.Module):
@@ -55,7 +57,7 @@ class QLoRALinear(torch.nn.Module):
     """
 
     def __init__(self, weight: torch.Tensor, r: int = 8, alpha: float = 16.0, freeze_A: bool = False,
-                 generator: torch.Generator | None = None, double_quant: bool = True):
+                 generator: torch.Generator | None = None, double_quant: bool = True, recompute_u: bool = False):
         super().__init__()
         if weight.dim() != 2:
             raise ValueError("weight must be [d_out, d_in]")
@@ -67,6 +69,7 @@ class QLoRALinear(torch.nn.Module):
         self.register_buffer("qscale", self.w.qscale, persistent=True)
         self.register_buffer("smax", self.w.smax, persistent=True)
         self.d_out, self.d_in, self.r, self.alpha = d_out, d_in, r, float(alpha)
+        self.recompute_u = recompute_u
         if r > 0:
             A = torch.randn(r, d_in, device=weight.device, generator=generator) * 0.02
             self.A = torch.nn.Parameter(A.to(torch.bfloat16), requires_grad=not freeze_A)
@@ -77,7 +80,7 @@ class QLoRALinear(torch.nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.d_in).to(torch.bfloat16).contiguous()
-        h = QLoRALinearFunction.apply(x2, self.A, self.B, self.w, self.alpha)
+        h = QLoRALinearFunction.apply(x2, self.A, self.B, self.w, self.alpha, self.recompute_u)
         return h.reshape(*lead, self.d_out)
 
     @torch.no_grad()

@@ -176,3 +176,33 @@ def test_two_chained_layers_match_oracle():
     assert_close("dA1", m1.A.grad, dA1)
     assert_close("dB1", m1.B.grad, dB1)
     assert_close("dX1", x.grad, dX1)
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_recompute_u_keeps_no_intermediate(T):
+    """recompute_u: the layer keeps x but not u, the backward forms u again, and the gradients match the oracle
+    (and the saved-u run within the same tolerance)."""
+    say(f"recompute_u T={T}")
+    case = Case(272, 320, 64, T, cfg=126)
+    d = case.device_inputs()
+    grads = {}
+    for rec in (False, True):
+        m = layer.QLoRALinear(d["W"], r=case.r, alpha=case.alpha, recompute_u=rec)
+        with torch.no_grad():
+            m.A.copy_(d["A"])
+            m.B.copy_(d["B"])
+        x = d["x"].clone().requires_grad_(True)
+        h = m(x)
+        node = h.grad_fn
+        while type(node).__name__ != "QLoRALinearFunctionBackward":
+            node = node.next_functions[0][0]
+        saved = node.saved_tensors
+        assert (saved[3] is None) == rec and saved[0] is not None
+        (h.float() * d["dY"].float()).sum().backward()
+        torch.cuda.synchronize()
+        grads[rec] = (x.grad.clone(), m.A.grad.clone(), m.B.grad.clone())
+    dX_ref, dA_ref, dB_ref = case.oracle_backward()
+    for rec in (False, True):
+        assert_close(f"dX rec={rec}", grads[rec][0], dX_ref)
+        assert_close(f"dA rec={rec}", grads[rec][1], dA_ref)
+        assert_close(f"dB rec={rec}", grads[rec][2], dB_ref)
