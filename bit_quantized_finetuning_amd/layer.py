@@ -157,5 +157,5 @@ class QLoRAFusedLinear(torch.nn.Module):
         A, B = self.stacked_adapter()
         n_ad = len(self.A)
         alpha = self.alpha * n_ad if n_ad else self.alpha  # scale alpha / (n_ad r) = self.alpha / r
-        h = QLoRALinearFunction.apply(x2, A, B, self.w, alpha)
+        h = QLoRALinearFunction.apply(x2, A, B, self.w, alpha, False)
         return tuple(t.reshape(*lead, t.shape[-1]) for t in torch.split(h, self.d_outs, dim=1))
