@@ -166,7 +166,12 @@ _workspaces: dict = {}
 
 
 def workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised workspace cached per device (the library leaves its counters zero after each call)."""
+    """A zero-initialised workspace cached per device (the library leaves its counters zero after each call).
+
+    The cached workspace is shared by every call on the device that does not pass its own: calls that may run
+    concurrently (on different streams) must pass distinct workspaces (`ws=`), each zeroed once, e.g. with
+    `torch.zeros(qlora_workspace_bytes(...), dtype=torch.uint8, device=...)`.
+    """
     dev = torch.device(device)
     key = (dev.type, dev.index)
     ws = _workspaces.get(key)
@@ -177,6 +182,12 @@ def workspace(device, nbytes: int) -> torch.Tensor:
         torch.cuda.synchronize(dev)
         ws = torch.zeros(size, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
+    return ws
+
+
+def _own_workspace(ws: torch.Tensor, nbytes: int) -> torch.Tensor:
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.numel() < nbytes:
+        raise ValueError(f"ws must be a contiguous uint8 tensor of at least {nbytes} bytes")
     return ws
 
 
@@ -255,7 +266,8 @@ def qlora_adamw_step(step: int, grad: torch.Tensor, master: torch.Tensor, m: tor
 
 
 def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
-                  save_u: bool = False, h: torch.Tensor | None = None, u: torch.Tensor | None = None):
+                  save_u: bool = False, h: torch.Tensor | None = None, u: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None):
     """h = x W_hat^T + (alpha/r) (x A^T) B^T. Returns (h, u); u is float32 [T, r] when save_u or given, else None.
 
     h and u may be passed in (preallocated outputs); otherwise they are allocated here.
@@ -270,7 +282,7 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
     if u is None and save_u and r > 0:
         u = torch.empty(T, r, dtype=torch.float32, device=x.device)
     nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
-    ws = workspace(x.device, nbytes)
+    ws = workspace(x.device, nbytes) if ws is None else _own_workspace(ws, nbytes)
     cw = w._c()
     _check(_lib.qlora_forward(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
                               _ptr(ws), ws.numel(), _stream(x.device)), "qlora_forward")
@@ -280,7 +292,8 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
 def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor | None,
                    B: torch.Tensor | None, alpha: float, u_saved: torch.Tensor | None = None,
                    need_dx: bool = True, need_dA: bool = True, need_dB: bool = True,
-                   dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None):
+                   dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None):
     """Returns (dX bf16 [T, d_in] | None, dA f32 [r, d_in] | None, dB f32 [d_out, r] | None).
 
     Outputs passed in are written in place (and count as needed); the others are allocated when needed.
@@ -296,7 +309,7 @@ def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: to
     if dB is None and need_dB and r > 0:
         dB = torch.empty(w.d_out, r, dtype=torch.float32, device=dev)
     nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
-    ws = workspace(dev, nbytes)
+    ws = workspace(dev, nbytes) if ws is None else _own_workspace(ws, nbytes)
     cw = w._c()
     _check(_lib.qlora_backward(ctypes.byref(cw), _ptr(x), _ptr(dY), T, _ptr(A), _ptr(B), r, alpha, _ptr(u_saved),
                                _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)), "qlora_backward")

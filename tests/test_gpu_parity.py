@@ -296,3 +296,42 @@ def test_merge_without_adapter_is_the_restore():
     torch.cuda.synchronize()
     for t in (plain, zero_b):
         assert np.array_equal(t.float().cpu().numpy(), wb)  # values; a -0.0 restore comes back +0.0
+
+
+def test_concurrent_streams_with_own_workspaces():
+    """Two skinny forwards (their adapter exchange runs through the workspace) and two GEMM backwards issued on two
+    streams at once, each with its own workspace, give bit for bit the results of the same calls run one after
+    the other."""
+    say("concurrent streams")
+    cases = [Case(1024, 1024, 64, 16, cfg=127, proj=i) for i in range(2)]
+    ins = []
+    for c in cases:
+        d = c.device_inputs()
+        ins.append((q.qlora_quantize(d["W"]), d))
+    torch.cuda.synchronize()
+
+    def run(k, ws=None):
+        w, d = ins[k]
+        h, u = q.qlora_forward(w, d["x"], d["A"], d["B"], 16.0, save_u=True, ws=ws)
+        x300 = d["x"].repeat(19, 1)[:300].contiguous()
+        dy300 = torch.cat([d["dY"]] * 19)[:300].contiguous()
+        g = q.qlora_backward(w, x300, dy300, d["A"], d["B"], 16.0, ws=ws)
+        return (h, u) + tuple(g)
+
+    ref = [run(0), run(1)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]   # default priority
+    wss = [torch.zeros(q.qlora_workspace_bytes(1024, 1024, 300, 64), dtype=torch.uint8, device="cuda")
+           for _ in range(2)]
+    torch.cuda.synchronize()
+    out = [None, None]
+    for k in range(2):
+        with torch.cuda.stream(streams[k]):
+            out[k] = run(k, wss[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        for a, b in zip(out[k], ref[k]):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    for ws in wss:
+        assert int(ws[:q.COUNTER_BYTES].view(torch.int32).abs().sum().item()) == 0
