@@ -2,7 +2,8 @@
 
     python -m bit_quantized_finetuning_amd.build [--verbose]
 
-Compiles every source under csrc/ into one shared library next to this file.
+Compiles every source under csrc/ (one object each, in parallel, under _build/)
+and links one shared library next to this file.
 Flags: correctly rounded float32 division (the quantizer's normalization must
 match an IEEE divide bit for bit), no packed-FP32 instruction selection, and no
 fast-math.
@@ -38,19 +39,42 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
+    """Compile every source to an object (in parallel, under _build/), then link libqlora.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-shared"] + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include")]
     t0 = time.time()
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, res, cmd
+
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    msgs = []
+    for obj, res, cmd in results:
+        out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                        if "packed-fp32-ops' is not a recognized feature" not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+        if out.strip():
+            msgs.append(out)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [r[0] for r in results]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out, flush=True)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)

@@ -165,6 +165,68 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP
 
 }  // namespace
 
+namespace qlora {
+
+// Argument checks of a forward call that do not involve the workspace.
+int validate_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
+                     int32_t r, uint16_t *h, float *u_out) {
+  int s = validate_weight(W);
+  if (s) return s;
+  if (!x || !h) return QLORA_ERR_NULL;
+  if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (T > kMaxTokens) return QLORA_ERR_SHAPE;
+  if (!A && !B) r = 0;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(h) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+      (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+// Workspace bytes one forward call touches (its counters, intermediates and
+// partials; qlora_workspace_bytes also covers the backward at the same sizes).
+size_t forward_workspace_need(int64_t d_out, int64_t d_in, int64_t T, int r) {
+  const Layout L = layout(d_out, d_in, T, r);
+  // the weight-streaming kernel uses the counters and the tagged exchange only
+  if (gemv_supported(d_out, d_in, T)) return L.u;
+  // the tiled path: counters, s*u, and the partials of u = x A^T and of the contraction's split tail
+  size_t pf = gemm_partial_floats(gemm_plan(T, d_out, d_in / kBlock));
+  if (r > 0)
+    pf = std::max(pf, T >= kWideMinTokens ? lora_tall_partial_floats(T, d_in, rank_pad(r))
+                                          : (size_t)ceil_div(T, 16) * lora_small_ksplit(T, d_in) * 16 * rank_pad(r));
+  return L.partial + pf * 4;
+}
+
+// The forward's kernels on a checked workspace (r already 0 when A = B = NULL).
+int enqueue_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
+                    int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, hipStream_t stream) {
+  const int64_t d_out = W->d_out, d_in = W->d_in;
+  const Layout L = layout(d_out, d_in, T, r);
+  const int rp = rank_pad(r);
+  const float sc = r > 0 ? alpha / (float)r : 0.f;
+  if (gemv_supported(d_out, d_in, T))
+    return hip_status(launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, A, B, r, rp, sc, h, u_out,
+                                      at<uint64_t>(ws, L.su32), at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4),
+                                      stream));
+  uint16_t *su = at<uint16_t>(ws, L.sx);
+  float *partial = at<float>(ws, L.partial);
+  hipError_t e = hipSuccess;
+  if (r > 0) {
+    if (T >= kWideMinTokens) {
+      e = launch_lora_tall(x, A, T, d_in, r, rp, sc, u_out, su, partial, at<uint32_t>(ws, 0), stream);
+    } else {
+      const int ks = lora_small_ksplit(T, d_in);
+      e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
+    }
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
+                      at<uint32_t>(ws, 0), stream);
+  return hip_status(e);
+}
+
+}  // namespace qlora
+
 extern "C" {
 
 void qlora_nf4_codebook(float out[16]) {
@@ -189,6 +251,13 @@ const char *qlora_status_string(int status) {
     case QLORA_ERR_VALUE: return "a hyperparameter is out of range (or step < 1)";
     default: return "unknown status";
   }
+}
+
+int qlora_workspace_fallbacks(const void *ws, uint32_t *count, hipStream_t stream) {
+  if (!ws || !count) return QLORA_ERR_NULL;
+  const void *word = static_cast<const uint8_t *>(ws) + (kMaxCounters - 1) * sizeof(uint32_t);
+  if (hipMemcpyAsync(count, word, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) return QLORA_ERR_HIP;
+  return hip_status(hipStreamSynchronize(stream));
 }
 
 size_t qlora_storage_bytes(int64_t d_out, int64_t d_in) {
@@ -304,43 +373,14 @@ int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, con
 int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
                   int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, size_t ws_bytes,
                   hipStream_t stream) {
-  int s = validate_weight(W);
+  int s = validate_forward(W, x, T, A, B, r, h, u_out);
   if (s) return s;
-  if (!x || !h) return QLORA_ERR_NULL;
-  if (T < 1 || r < 0 || r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_ERR_SHAPE;
-  if (T > kMaxTokens) return QLORA_ERR_SHAPE;
   if (!A && !B) r = 0;
-  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
-  if (!aligned16(x) || !aligned16(h) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
-      (u_out && !aligned16(u_out)))
-    return QLORA_ERR_ALIGN;
-  const int64_t d_out = W->d_out, d_in = W->d_in;
-  const Layout L = layout(d_out, d_in, T, r);
+  const Layout L = layout(W->d_out, W->d_in, T, r);
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   if (!ws) return QLORA_ERR_NULL;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
-
-  const int rp = rank_pad(r);
-  const float sc = r > 0 ? alpha / (float)r : 0.f;
-  if (gemv_supported(d_out, d_in, T))
-    return hip_status(launch_gemv_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, A, B, r, rp, sc, h, u_out,
-                                      at<uint64_t>(ws, L.su32), at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4),
-                                      stream));
-  uint16_t *su = at<uint16_t>(ws, L.sx);
-  float *partial = at<float>(ws, L.partial);
-  hipError_t e = hipSuccess;
-  if (r > 0) {
-    if (T >= kWideMinTokens) {
-      e = launch_lora_tall(x, A, T, d_in, r, rp, sc, u_out, su, partial, at<uint32_t>(ws, 0), stream);
-    } else {
-      const int ks = lora_small_ksplit(T, d_in);
-      e = launch_lora_small(x, A, T, d_in, r, sc, u_out, su, rp, partial, at<uint32_t>(ws, 0), ks, stream);
-    }
-    if (e != hipSuccess) return QLORA_ERR_HIP;
-  }
-  e = launch_gemm_fwd(W->codes, W->qscale, W->smax, d_out, d_in, x, T, su, rp, B, r, h, partial,
-                      at<uint32_t>(ws, 0), stream);
-  return hip_status(e);
+  return enqueue_forward(W, x, T, A, B, r, alpha, h, u_out, ws, stream);
 }
 
 int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t *dY, int64_t T, const uint16_t *A,
@@ -392,10 +432,10 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   const bool wide = T >= kWideMinTokens;
-  uint32_t *err = at<uint32_t>(ws, (kMaxCounters - 1) * 4);
+  uint32_t *fallbacks = at<uint32_t>(ws, (kMaxCounters - 1) * 4);
   if (dA) {
     if (wide)
-      e = launch_lora_wgrad(x, v, T, d_in, r, true, sc, dA, partial, at<uint32_t>(ws, 0), err, stream);
+      e = launch_lora_wgrad(x, v, T, d_in, r, true, sc, dA, partial, at<uint32_t>(ws, 0), fallbacks, stream);
     else
       e = launch_lora_grad(v, true, r, x, false, d_in, T, sc, dA, partial, at<uint32_t>(ws, 0),
                            lora_grad_ksplit(r, d_in, T), stream);
@@ -413,7 +453,7 @@ int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t 
       u = uw;
     }
     if (wide)
-      e = launch_lora_wgrad(dY, u, T, d_out, r, false, sc, dB, partial, at<uint32_t>(ws, 0), err, stream);
+      e = launch_lora_wgrad(dY, u, T, d_out, r, false, sc, dB, partial, at<uint32_t>(ws, 0), fallbacks, stream);
     else
       e = launch_lora_grad(dY, false, d_out, u, true, r, T, sc, dB, partial, at<uint32_t>(ws, 0),
                            lora_grad_ksplit(d_out, r, T), stream);

@@ -38,9 +38,10 @@ __host__ __device__ inline int64_t scale_words(int64_t nblocks, int sshift) {
 // of all tiles arrive and poll at about the same time, and counters that share
 // a line serialize at one memory channel (measured: a third of a K-split
 // gradient kernel's time). A kernel whose tile count exceeds kMaxTileCounters
-// runs without a split. The last kSyncWords words of the region are reserved
-// for the skinny forward; the last of them is set if one of its bounded waits
-// timed out.
+// runs without a split. The last kSyncWords words of the region are reserved:
+// the last of them counts the waits that ran out of time and took their
+// fallback (the result is the same either way; see split_claim and the skinny
+// forward's exchange).
 constexpr int64_t kMaxCounters = 16384;
 constexpr int64_t kSyncWords = 4;
 constexpr int64_t kCounterStride = 32;  // 32-bit words per tile counter
@@ -229,6 +230,75 @@ __device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
 }
 __device__ __forceinline__ uint32_t add_dev_u32(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t xchg_dev_u32(uint32_t *p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// How long a workgroup waits for others of its launch before it takes a path
+// that needs no one else: 20000 ticks of the constant 100 MHz counter that
+// wall_clock64() reads, about 200 us. Within one launch on an idle chip every
+// wait ends in a few microseconds; the limit matters only when launches on
+// other streams hold the compute units that the awaited workgroups need.
+constexpr long long kWaitTicks = 20000;
+
+// ---------------------------------------------------------------------------
+// Combine of a tile whose reduction range is split over `parts` workgroups,
+// with no wait that progress depends on. Every part stores its float32 partial
+// (device scope, complete before it arrives) and the tile's sum is cut into
+// `parts` shares, each summed over all partials in part order (so the result
+// does not depend on who sums it). The tile's counter line holds:
+//   word 0        arrivals (low 16 bits) and departures (high 16 bits)
+//   word 1 + s    claim of share s (0 free, 1 taken)
+// A part that arrives last knows every partial is stored; an earlier part
+// polls for the last arrival until kWaitTicks pass. Whoever has seen all
+// arrivals claims its own share (one atomic exchange) and sums it if the claim
+// wins; the last arriver afterwards claims every share still free and sums
+// those too. So every share is summed exactly once, by its own part when all
+// parts run together, and by the last arriver for the parts that gave up
+// waiting (a wait then costs time, never a wrong or missing result). The last
+// part to depart clears the line for the next launch on the workspace.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kDepart = 0x10000u;
+
+// Thread-0 side of the arrival: returns the claimed-share mask of this part
+// (own share only; the last arriver's sweep comes later) and whether it
+// arrived last. `fallbacks` counts waits that ran out of time.
+__device__ __forceinline__ uint32_t split_arrive(uint32_t *line, int part, int parts, bool &last,
+                                                 uint32_t *fallbacks) {
+  const uint32_t prev = add_dev_u32(line, 1u);
+  last = (prev & 0xffffu) == (uint32_t)(parts - 1);
+  bool ready = last;
+  if (!last) {
+    const long long t0 = wall_clock64();
+    for (;;) {
+      if ((ld_dev_u32(line) & 0xffffu) >= (uint32_t)parts) {
+        ready = true;
+        break;
+      }
+      if (wall_clock64() - t0 > kWaitTicks) {
+        add_dev_u32(fallbacks, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  return ready && xchg_dev_u32(line + 1 + part, 1u) == 0u ? 1u << part : 0u;
+}
+// The last arriver's sweep, run by one whole wave (lane p claims share p, all
+// in one round trip): the mask of the shares it won.
+__device__ __forceinline__ uint32_t split_sweep(uint32_t *line, int part, int parts, int lane) {
+  bool won = false;
+  if (lane < parts && lane != part) won = xchg_dev_u32(line + 1 + lane, 1u) == 0u;
+  return (uint32_t)__ballot(won);
+}
+// Thread 0, after every claim of this part is settled: count the departure;
+// the last one out clears the line.
+__device__ __forceinline__ void split_depart(uint32_t *line, int parts) {
+  if ((add_dev_u32(line, kDepart) >> 16) == (uint32_t)(parts - 1)) {
+    for (int p = 0; p < parts; ++p) st_dev_u32(line + 1 + p, 0u);
+    st_dev_u32(line, 0u);
+  }
 }
 // A 32-bit name of the running launch: the dispatch id (the queue's packet
 // counter, which advances for every launch, graph replays included) mixed with

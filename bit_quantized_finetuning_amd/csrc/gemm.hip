@@ -302,22 +302,20 @@ __device__ __forceinline__ WorkItem work_item(int gn, int nk, int full, int spli
   return w;
 }
 
-// End of a K part of a tail tile. Every part stores its float32 tile
-// (device-scope stores, written through to memory), counts itself in, and
-// waits (bounded) until all parts of the tile have; then part p sums row
-// tiles [8p/parts, 8(p+1)/parts) of all parts, in part order (device-scope
-// loads; the sum does not depend on which part finished first), and stages
-// those rows as bf16 for the caller to store. A second count lets the last
-// part out reset the counter for the next launch. Wave w's accumulators sit
-// at floats [16384 w, 16384 (w+1)) of a part's tile as 64 chunks of 1 KB,
-// lane-major. The parts of a tile are consecutive workgroups: when they do not
-// all fit on the chip at once, the ones waiting hold their compute units only
-// until the earlier tiles' parts finish. A wait that runs out sets the
-// workspace's error word and goes on (the tile is then wrong, nothing hangs).
-constexpr int kSpinLimit = 1 << 20;
+// End of a K part of a tail tile (the combine protocol of split_arrive in
+// common.h). Every part stores its float32 tile with device-scope stores and
+// arrives; share p of the tile is row tiles [8p/parts, 8(p+1)/parts), summed
+// over all parts in part order by whichever workgroup claims it, staged as
+// bf16 and handed to store_rows(rlo, rhi). Wave w's accumulators sit at floats
+// [16384 w, 16384 (w+1)) of a part's tile as 64 chunks of 1 KB, lane-major;
+// each wave sums and stores its own 64 columns. No part depends on another
+// part being dispatched: one that stops waiting leaves its share to the last
+// arriver.
+template <typename StoreRows>
 __device__ __forceinline__ void split_combine(const f32x16 (&acc)[8][2], float *tile_parts, int part, int parts,
-                                              uint32_t *counter, uint32_t *err, uint16_t *stage, int tid, int wave,
-                                              int lane) {
+                                              uint32_t *line, uint32_t *fallbacks, uint16_t *stage, int tid,
+                                              int wave, int lane, StoreRows store_rows) {
+  __shared__ uint32_t claim_lds[2];
   const rsrc_t pr = make_rsrc(tile_parts, (int64_t)parts * kTileFloats * 4);
   const uint32_t lane_off = (uint32_t)(wave * (kTileFloats / 4) + 4 * lane) * 4u;
 #pragma unroll
@@ -333,46 +331,57 @@ __device__ __forceinline__ void split_combine(const f32x16 (&acc)[8][2], float *
       }
   wait_barrier<0>();  // every wave's stores have completed
   if (tid == 0) {
-    add_dev_u32(counter, 1u);
-    int it = 0;
-    while (ld_dev_u32(counter) < (uint32_t)parts) {
-      if (++it >= kSpinLimit) {
-        st_dev_u32(err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+    bool last;
+    claim_lds[0] = split_arrive(line, part, parts, last, fallbacks);
+    claim_lds[1] = last ? 1u : 0u;
   }
   wait_barrier<0>();
-  const int ilo = part * 8 / parts, ihi = (part + 1) * 8 / parts;
-  for (int i = ilo; i < ihi; ++i) {
-    f32x4 sum[2][4];
+  auto sum_shares = [&](uint32_t mask) {
+    for (int sh = 0; sh < parts; ++sh) {
+      if (!((mask >> sh) & 1u)) continue;
+      const int ilo = sh * 8 / parts, ihi = (sh + 1) * 8 / parts;
+      for (int i = ilo; i < ihi; ++i) {
+        f32x4 sum[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) sum[j][e4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < parts; ++p) {
-      u32x4 v[2][4];
+          for (int e4 = 0; e4 < 4; ++e4) sum[j][e4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < parts; ++p) {
+          u32x4 v[2][4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
-          v[j][e4] = bld16_dev(pr, (uint32_t)(p * kTileFloats) * 4u + lane_off + (uint32_t)((i * 2 + j) * 4 + e4) * 1024u);
+            for (int e4 = 0; e4 < 4; ++e4)
+              v[j][e4] = bld16_dev(pr, (uint32_t)(p * kTileFloats) * 4u + lane_off + (uint32_t)((i * 2 + j) * 4 + e4) * 1024u);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
+            for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) sum[j][e4][u] += __uint_as_float(v[j][e4][u]);
+              for (int u = 0; u < 4; ++u) sum[j][e4][u] += __uint_as_float(v[j][e4][u]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            stage_put4(stage, lane, i, j, e4, sum[j][e4][0], sum[j][e4][1], sum[j][e4][2], sum[j][e4][3]);
+      }
+      store_rows(32 * ilo, 32 * ihi);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        stage_put4(stage, lane, i, j, e4, sum[j][e4][0], sum[j][e4][1], sum[j][e4][2], sum[j][e4][3]);
+  };
+  const uint32_t mine = claim_lds[0];
+  const bool last = claim_lds[1] != 0u;
+  sum_shares(mine);
+  if (last) {
+    wait_barrier<0>();  // every wave has read the claim words
+    if (wave == 0) {
+      const uint32_t m = split_sweep(line, part, parts, lane);
+      if (lane == 0) claim_lds[0] = m;
+    }
+    wait_barrier<0>();
+    sum_shares(claim_lds[0]);
   }
-  wait_vmem();
-  if (tid == 0 && add_dev_u32(counter, 1u) == (uint32_t)(2 * parts - 1)) st_dev_u32(counter, 0u);
+  if (tid == 0) split_depart(line, parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,16 +545,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   // Epilogue through LDS once every wave is done with the ring.
   wait_barrier<0>();
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * kBM * kEP;
-  int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
   if (wi.parts > 1) {
     split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
-                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
-    rlo = 32 * (wi.part * 8 / wi.parts);
-    rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
+                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane,
+                  [&](int rlo, int rhi) { stage_store(stage, lane, h, d_out, m0, n0 + kWN * wave, T, d_out, rlo, rhi); });
   } else {
     stage_acc(acc, stage, lane);
+    stage_store(stage, lane, h, d_out, m0, n0 + kWN * wave, T, d_out, 0, kBM);
   }
-  stage_store(stage, lane, h, d_out, m0, n0 + kWN * wave, T, d_out, rlo, rhi);
 }
 
 // ---------------------------------------------------------------------------
@@ -746,16 +753,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
 
   wait_barrier<0>();
   uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * kBM * kEP;
-  int rlo = 0, rhi = kBM;  // rows of the tile this workgroup stores
   if (wi.parts > 1) {
     split_combine(acc, partial + (size_t)(wi.tile - full) * split * kTileFloats, wi.part, wi.parts,
-                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane);
-    rlo = 32 * (wi.part * 8 / wi.parts);
-    rhi = 32 * ((wi.part + 1) * 8 / wi.parts);
+                  tile_counter(counters, wi.tile - full), counters + kMaxCounters - 1, stage, tid, wave, lane,
+                  [&](int rlo, int rhi) { stage_store(stage, lane, dX, d_in, m0, n0 + kWN * wave, T, d_in, rlo, rhi); });
   } else {
     stage_acc(acc, stage, lane);
+    stage_store(stage, lane, dX, d_in, m0, n0 + kWN * wave, T, d_in, 0, kBM);
   }
-  stage_store(stage, lane, dX, d_in, m0, n0 + kWN * wave, T, d_in, rlo, rhi);
 }
 
 static bool g_attr_set[64];

@@ -22,7 +22,8 @@
 //     so that the CUs, which all read all of x, spread over the L2 channels.
 //     Otherwise x is read per segment from global memory. Loads go out in the
 //     order they are needed (they complete in issue order).
-//   * the last P = 4 r_pad/16 workgroups (those with the fewest row tiles)
+//   * the first P = 4 r_pad/16 workgroups (dispatched first, and given the
+//     fewest row tiles: workgroup c streams row tiles G-1-c, 2G-1-c, ...)
 //     also produce the adapter intermediate: producer (j, ks) forms the
 //     partial of columns 16j..16j+15 of u = x A^T over the ks-th quarter of K
 //     (a single CU streams only a few tens of GB/s, so the A reads are
@@ -38,12 +39,18 @@
 //     or, across queues, with probability 2^-32 per change of queue.
 //   * s*u is read once per workgroup: the loads go out before the last item of
 //     the first row tile, and at that tile's end the entries are checked (and
-//     re-read until their tags match, with a bounded wait), the four partials
-//     summed in slice order and bf16(s*u) put in LDS; wave 0 then adds s*u B^T
-//     as r_pad more K columns. Workgroup 0 writes float32 u for the backward.
+//     re-read until their tags match), the four partials summed in slice order
+//     and bf16(s*u) put in LDS; wave 0 then adds s*u B^T as r_pad more K
+//     columns. The workgroup of row tile 0 writes float32 u for the backward.
+//   * a reader that has waited kWaitTicks for a partial forms it itself with
+//     the producer's own code (same operands, same order of operations, so the
+//     same bits) and publishes it as the producer would. The grid never
+//     exceeds one residency and producers never wait, so on its own a launch
+//     never gets there; when launches on other streams hold the compute units
+//     a producer needs, this keeps every wait finite and every result exact.
+//     Each such fallback is counted in a status word of the workspace.
 //   * at the end of a row tile the waves reduce through LDS and write h.
-// The grid never exceeds one residency, producers never wait for anyone, and
-// the one wait is bounded (timeout -> status word, never a hang). Buffer
+// Buffer
 // descriptors cover whole tensors (the launcher requires the packed codes to
 // stay below 2^31 bytes); per-lane offsets are 32-bit and an out-of-range lane
 // reads zero.
@@ -51,7 +58,6 @@
 
 namespace qlora {
 
-constexpr int kSpinLimit = 1 << 20;  // bounded wait; only a safety net
 constexpr int kMaxRpad = 256;
 constexpr int kXPad = 8;             // bf16 of padding per staged x row (rows 4 banks apart)
 constexpr int kXLdsBytes = 136 * 1024;
@@ -86,6 +92,8 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   __shared__ float red[kW][256];
   __shared__ __attribute__((aligned(16))) uint16_t su_l[16 * kMaxRpad];
   __shared__ int poll_bad[2][kW];
+  __shared__ int poll_late[2];
+  __shared__ uint32_t miss[2];  // jobs with a partial not yet seen (bit j kKsp + ks)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int li = lane & 15, g = lane >> 4;
   const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
@@ -93,7 +101,8 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   const int cid = blockIdx.x, G = gridDim.x;
   const int xpitch = d_in + kXPad;
   const int RT = (d_out + 15) / 16;
-  const int nrt = cid < RT ? (RT - cid + G - 1) / G : 0;
+  const int rt0 = G - 1 - cid;  // row tiles rt0, rt0 + G, ... (the producers, first, get the fewest)
+  const int nrt = rt0 < RT ? (RT - rt0 + G - 1) / G : 0;
   const int NS = (KB + 3) / 4;
   // Segments seg = wv + kW s of every row tile belong to wave slot wv; the slot
   // is rotated per workgroup so that at any moment different workgroups read
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   // Item (row tile k, segment s): lane (li, g) takes block g of the segment in
   // row 16 (c + kG) + li. Rows past d_out (ragged tile, k >= nrt) read zeros.
   auto load_codes = [&](int k, int s, GemvCodes &st) {
-    const int row = (cid + k * G) * 16 + li;
+    const int row = (rt0 + k * G) * 16 + li;
     const int kb = 4 * (wv + kW * s) + g;
     const bool ok = row < d_out && kb < KB;
     const uint32_t blk = (uint32_t)row * (uint32_t)KB + (uint32_t)kb;
@@ -133,19 +142,18 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   // Loads complete in issue order, so everything a step waits for goes out
   // before the loads it does not need yet.
 
-  // producer (j, ks): A rows 16j..16j+15 over K slice ks (steps of 32 split
-  // over the waves). A CU streams only a few tens of GB/s on its own, so the
-  // A reads are spread over kKsp producers per column tile. Producers are the
-  // last P workgroups, which hold the fewest row tiles.
-  const int pid = cid - (G - P);
-  const bool producer = P > 0 && pid >= 0;
-  const int pj = producer ? pid / kKsp : 0, pks = producer ? pid % kKsp : 0;
+  // Job (j, ks) = id j kKsp + ks: the partial of u columns 16j..16j+15 over K
+  // slice ks (A rows 16j..16j+15; steps of 32 split over the waves). A CU
+  // streams only a few tens of GB/s on its own, so the A reads are spread over
+  // kKsp producers per column tile. Producer workgroup c runs job c.
+  const bool producer = P > 0 && cid < P;
   const int nk32 = d_in / 32;
-  const int k32b = producer ? nk32 * pks / kKsp : 0, k32e = producer ? nk32 * (pks + 1) / kKsp : 0;
-  const int arows = producer ? (r - 16 * pj < 16 ? r - 16 * pj : 16) : 0;
-  const rsrc_t ar = make_rsrc(A + (producer ? (int64_t)16 * pj * d_in : 0), (int64_t)arows * d_in * 2);
   u32x4 ap[kABatch], xp[kABatch];
-  auto a_issue = [&](int b) {
+  auto a_issue = [&](int job, int b) {
+    const int pj = job / kKsp, pks = job % kKsp;
+    const int k32b = nk32 * pks / kKsp, k32e = nk32 * (pks + 1) / kKsp;
+    const int arows = r - 16 * pj < 16 ? r - 16 * pj : 16;
+    const rsrc_t ar = make_rsrc(A + (int64_t)16 * pj * d_in, (int64_t)arows * d_in * 2);
 #pragma unroll
     for (int s = 0; s < kABatch; ++s) {
       const int k32 = k32b + wave + kW * (kABatch * b + s);
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       }
   };
   // A producer's own operands go out first: its job needs nothing else.
-  if (producer) a_issue(0);
+  if (producer) a_issue(cid, 0);
   if (kXL && mseg > 0) x_issue(0);
 
   // Items (row tile k, segment s) in order k * mseg + s, through a ring of
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   u32x4 bpre[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   const rsrc_t br = make_rsrc(B, (int64_t)d_out * r * 2);
   auto load_b = [&](int k) {
-    const int row = (cid + k * G) * 16 + li;
+    const int row = (rt0 + k * G) * 16 + li;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int j = 32 * q + 8 * g;
@@ -230,21 +238,22 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   if (P > 0 && wave == 0) load_b(0);
 
   // ---------------- adapter producer job ----------------
-  // The partial of columns 16j..16j+15 of u = x A^T over K slice ks: the
-  // waves split the slice and reduce through LDS; each float32 value goes out
-  // with this launch's tag in one 64-bit store. Nothing waits for those
-  // stores: a reader accepts an entry once its tag matches.
+  // The partial of columns 16j..16j+15 of u = x A^T over K slice ks, with the
+  // loads of its first batch already issued: the waves split the slice and
+  // reduce through LDS; each float32 value goes out with this launch's tag in
+  // one 64-bit store. Nothing waits for those stores: a reader accepts an
+  // entry once its tag matches. (Run by every wave of the workgroup.)
   const uint32_t tag = launch_tag();
-  // x comes straight from global memory (rows >= T read zeros), so the job
-  // waits for nothing but its own loads, issued first.
-  if (producer) {
+  auto a_run = [&](int job) {
+    const int pj = job / kKsp, pks = job % kKsp;
+    const int k32b = nk32 * pks / kKsp, k32e = nk32 * (pks + 1) / kKsp;
     f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
     for (int b = 0;; ++b) {
 #pragma unroll
       for (int s = 0; s < kABatch; ++s)
         if (k32b + wave + kW * (kABatch * b + s) < k32e) pacc = mfma16(xp[s], ap[s], pacc);  // wave-uniform
       if (k32b + kABatch * kW * (b + 1) >= k32e) break;
-      a_issue(b + 1);
+      a_issue(job, b + 1);
     }
     // lane (li, g) holds u[4g + i][16j + li]
 #pragma unroll
@@ -258,7 +267,10 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       if (t < T) st_dev_u64(uex + (pks * 16 + t) * r_pad + col, (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32));
     }
     lds_barrier();
-  }
+  };
+  // x comes straight from global memory (rows >= T read zeros), so the job
+  // waits for nothing but its own loads, issued first.
+  if (producer) a_run(cid);
 
   if (kXL && mseg > 0) {
     x_store(0);
@@ -313,17 +325,21 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
 
   // Row-tile epilogue: adapter columns (wave 0), LDS reduce across waves, store h.
   auto epilogue = [&](int k) {
-    const int row0 = (cid + k * G) * 16;
+    const int row0 = (rt0 + k * G) * 16;
     const int rows = d_out - row0 < 16 ? d_out - row0 : 16;
     if (P > 0 && k == 0) {
       // bf16(s*u) rows t < T into LDS once every tag matches: u is the sum of
-      // the kKsp partials in slice order (the same on every workgroup);
-      // workgroup 0 also writes float32 u. Rows t >= T of su_l only feed
-      // accumulator rows that are never stored.
+      // the kKsp partials in slice order (the same on every workgroup); the
+      // workgroup of row tile 0 also writes float32 u. Rows t >= T of su_l
+      // only feed accumulator rows that are never stored.
       // One round: write every entry whose partials all carry this launch's
-      // tag; returns whether any entry of the workgroup was not ready (two
-      // flag rows in turn: a row is rewritten only two barriers after it was
-      // last read).
+      // tag, note the jobs of those that do not, and (thread 0) whether the
+      // wait has run out of time; returns whether any entry of the workgroup
+      // was not ready (two flag rows in turn: a row is rewritten only two
+      // barriers after it was last read).
+      const long long t0 = wall_clock64();
+      if (tid == 0) miss[0] = miss[1] = 0u;
+      lds_barrier();
       auto check = [&](const uint64_t (&pv)[kPairsAhead][kKsp], int it) {
         int bad = 0;
         for (int i = 0; i * kThreads < npair; ++i) {
@@ -339,7 +355,12 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
           float u = 0.f;
 #pragma unroll
           for (int ks = 0; ks < kKsp; ++ks) {
-            ok = ok && (uint32_t)(e[ks] >> 32) == tag;
+            const bool oks = (uint32_t)(e[ks] >> 32) == tag;
+            ok = ok && oks;
+            if (!oks) {
+              const int job = ((p - (p / r_pad) * r_pad) >> 4) * kKsp + ks;
+              atomicOr(&miss[job >> 5], 1u << (job & 31));
+            }
             u += __uint_as_float((uint32_t)e[ks]);
           }
           if (!ok) {
@@ -347,11 +368,12 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
           } else if (p < npair) {
             const int t = p / r_pad, col = p - t * r_pad;
             su_l[t * r_pad + col] = (uint16_t)(pack_bf16x2(col < r ? scale * u : 0.f, 0.f) & 0xffffu);
-            if (u_out && cid == 0 && col < r) u_out[t * r + col] = u;
+            if (u_out && rt0 == 0 && col < r) u_out[t * r + col] = u;
           }
         }
         const int wbad = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0ull ? 1 : 0);
         if (lane == 0) poll_bad[it & 1][wave] = wbad;
+        if (tid == 0) poll_late[it & 1] = wall_clock64() - t0 > kWaitTicks ? 1 : 0;
         lds_barrier();
         int any = 0;
 #pragma unroll
@@ -361,11 +383,24 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       if (!polled) poll_issue(pv0);
       for (int it = 0;; ++it) {
         if (!check(pv0, it)) break;
-        if (it >= kSpinLimit) {
-          if (tid == 0) st_dev_u32(&sync[3], 1u);
-          break;
+        if (poll_late[it & 1]) {
+          // form the missing partials here, exactly as their producers would,
+          // and publish them; the next round then finds every entry
+          const uint32_t m0 = miss[0], m1 = miss[1];
+          for (int job = 0; job < P; ++job) {
+            if (!(((job < 32 ? m0 : m1) >> (job & 31)) & 1u)) continue;
+            a_issue(job, 0);
+            a_run(job);
+          }
+          if (tid == 0) {
+            miss[0] = miss[1] = 0u;
+            add_dev_u32(&sync[3], 1u);
+          }
+          wait_vmem();  // the published entries are in memory before anyone polls again
+          lds_barrier();
+        } else {
+          __builtin_amdgcn_s_sleep(2);
         }
-        __builtin_amdgcn_s_sleep(2);
         poll_issue(pv0);
       }
     }
@@ -463,7 +498,8 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
   const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
   const int64_t RT = (d_out + 15) / 16;
   // One workgroup per CU; the first P of them also produce x A^T. The grid never
-  // exceeds one residency, so every workgroup runs concurrently.
+  // exceeds one residency, so on an otherwise idle chip every workgroup runs
+  // concurrently (the kernel does not depend on it: see the file comment).
   int64_t G = RT < device_cus(dev) ? RT : device_cus(dev);
   if (G < P) G = P;
   const size_t xbytes = (size_t)T * (d_in + kXPad) * 2;

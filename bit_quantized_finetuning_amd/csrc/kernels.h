@@ -6,8 +6,18 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "qlora.h"
 
 namespace qlora {
+
+// api.cpp: the forward's argument checks, the workspace bytes one forward call
+// touches, and its kernels on a checked workspace (used by the entry points of
+// api.cpp and scratch.hip). r must already be 0 when A = B = NULL for the last two.
+int validate_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
+                     int32_t r, uint16_t *h, float *u_out);
+size_t forward_workspace_need(int64_t d_out, int64_t d_in, int64_t T, int r);
+int enqueue_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
+                    int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, hipStream_t stream);
 
 // quantize.hip
 hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d_in, uint8_t *codes,
@@ -47,7 +57,8 @@ hipError_t launch_transpose_bf16(const uint16_t *src, int64_t rows, int64_t cols
 // h[T, d_out] = x W_hat^T + scale (x A^T) B^T. u_out (nullable) receives x A^T
 // [T, r]. uex is the [4, 16, r_pad] exchange buffer of tagged float32 partials
 // of x A^T (one per quarter of K); sync points at four reserved words (word 3
-// is set if a bounded wait timed out).
+// counts the workgroups whose wait for a partial ran out of time and which then
+// formed it themselves; the result does not depend on it).
 hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out,
                            int64_t d_in, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B, int r,
                            int r_pad, float scale, uint16_t *h, float *u_out, uint64_t *uex, uint32_t *sync,
@@ -60,8 +71,8 @@ bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T);
 // nk K steps of 64 each): tiles 0 .. full-1 run whole, one workgroup each; each
 // of the remaining `rem` tiles is cut into `split` K ranges run by separate
 // workgroups, which store their float32 partial tiles (gemm_partial_floats in
-// total, in the workspace's shared scratch region), wait for each other
-// (bounded) and each sum a share of the tile's rows in range order. Chosen so
+// total, in the workspace's shared scratch region) and sum the tile's rows in
+// range order, one share each (split_arrive in common.h). Chosen so
 // that the chip's last round of tiles is not left mostly idle; depends on the
 // current device's compute-unit count.
 struct GemmPlan {
@@ -90,10 +101,10 @@ hipError_t launch_lora_tall(const uint16_t *P, const uint16_t *Q, int64_t T, int
 size_t lora_tall_partial_floats(int64_t T, int64_t K, int r_pad);
 // X bf16 [T, D], Y float32 [T, R]. y_is_rows: C[R, D] = scale * Y^T X (dA);
 // otherwise C[D, R] = scale * X^T Y (dB). Uses `partial`
-// (lora_wgrad_partial_floats), `counters` (one tile_counter per output tile) and sets *err
-// if a bounded wait ran out.
+// (lora_wgrad_partial_floats) and `counters` (one tile_counter per output tile); counts in
+// *fallbacks the waits that ran out of time (the result does not depend on them).
 hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64_t D, int64_t R, bool y_is_rows,
-                             float scale, float *C, float *partial, uint32_t *counters, uint32_t *err,
+                             float scale, float *C, float *partial, uint32_t *counters, uint32_t *fallbacks,
                              hipStream_t st);
 size_t lora_wgrad_partial_floats(int64_t D, int64_t R, int64_t T);
 

@@ -24,8 +24,10 @@
 // (64 x 512 bytes) and the Y tile (64 x 256 bytes) are copied into LDS two
 // steps ahead, and the Y tile is converted in place into two bf16 planes. Both MFMA operands need 8 consecutive tokens per lane, which
 // ds_read_b64_tr_b16 gathers from the token-major tiles. Token ranges of one
-// tile are summed cooperatively: every range stores its float32 tile, waits
-// (bounded) for the others, and sums its share of rows in range order.
+// tile are summed cooperatively: every range stores its float32 tile and sums
+// its share of rows over all ranges in range order once all have arrived; a
+// range that stops waiting leaves its share to the last one to arrive
+// (split_arrive in common.h), so no range depends on another being dispatched.
 #include "kernels.h"
 #include "tiles.h"
 
@@ -255,7 +257,6 @@ constexpr int kWgSlot = kXTile + 2 * kYPlane;  // X tile + float32 Y tile (later
 constexpr int kWgRing = 3;            // two steps in flight
 constexpr int kWgTileFloats = kWgD * kWgR;
 constexpr size_t kWgLds = (size_t)kWgRing * kWgSlot;
-constexpr int kWgSpinLimit = 1 << 20;
 constexpr int kWgMaxSplit = 16;
 constexpr int kWgCopies = 8 + 4;      // 1 KB copies per wave per step: X, then Y
 
@@ -273,7 +274,7 @@ template <bool kYisA>
 __global__ __launch_bounds__(256) void k_lora_wgrad(const uint16_t *__restrict__ X, const float *__restrict__ Y,
                                                     int64_t T, int64_t D, int64_t R, float scale,
                                                     float *__restrict__ C, float *__restrict__ partial,
-                                                    uint32_t *__restrict__ counters, uint32_t *__restrict__ err,
+                                                    uint32_t *__restrict__ counters, uint32_t *__restrict__ fallbacks,
                                                     int ksplit) {
   // Ring slot: [X tile 64 x 512 B][Y: float32 64 x 256 B as copied, then in
   // place the bf16 high plane (first 8 KB) and low plane (next 8 KB)].
@@ -447,48 +448,61 @@ __global__ __launch_bounds__(256) void k_lora_wgrad(const uint16_t *__restrict__
         __builtin_amdgcn_raw_buffer_store_b128(v, prs, (uint32_t)((part * kWgTileFloats + 4 * g) * 4), 0, 16);
       }
   wait_barrier<0>();  // every wave's stores have completed
+  // Share p of the tile is chunks [p N / ksplit, (p+1) N / ksplit) (N chunks of
+  // four rows of one column, in the accumulator layout above), summed over all
+  // ranges in range order by whichever workgroup claims it (split_arrive).
+  __shared__ uint32_t claim_lds[2];
+  uint32_t *line = tile_counter(counters, tile);
   if (tid == 0) {
-    add_dev_u32(tile_counter(counters, tile), 1u);
-    int it = 0;
-    while (ld_dev_u32(tile_counter(counters, tile)) < (uint32_t)ksplit) {
-      if (++it >= kWgSpinLimit) {
-        st_dev_u32(err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+    bool last;
+    claim_lds[0] = split_arrive(line, part, ksplit, last, fallbacks);
+    claim_lds[1] = last ? 1u : 0u;
   }
   wait_barrier<0>();
-  // Range `part` sums chunks [glo, ghi) of all ranges; chunk g holds rows
-  // r .. r+3 of one column (the accumulator layout above).
-  const int glo = part * (kWgTileFloats / 4) / ksplit, ghi = (part + 1) * (kWgTileFloats / 4) / ksplit;
-  for (int g = glo + tid; g < ghi; g += 256) {
-    u32x4 w[kWgMaxSplit];
+  auto sum_shares = [&](uint32_t mask) {
+    for (int sh = 0; sh < ksplit; ++sh) {
+      if (!((mask >> sh) & 1u)) continue;
+      const int glo = sh * (kWgTileFloats / 4) / ksplit, ghi = (sh + 1) * (kWgTileFloats / 4) / ksplit;
+      for (int g = glo + tid; g < ghi; g += 256) {
+        u32x4 w[kWgMaxSplit];
 #pragma unroll
-    for (int p = 0; p < kWgMaxSplit; ++p)
-      if (p < ksplit) w[p] = bld16_dev(prs, (uint32_t)((p * kWgTileFloats + 4 * g) * 4));
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < kWgMaxSplit; ++p)
+          if (p < ksplit) w[p] = bld16_dev(prs, (uint32_t)((p * kWgTileFloats + 4 * g) * 4));
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < kWgMaxSplit; ++p)
-      if (p < ksplit)
-        v += f32x4{__uint_as_float(w[p][0]), __uint_as_float(w[p][1]), __uint_as_float(w[p][2]),
-                   __uint_as_float(w[p][3])};
-    const int gl = g & 63, e4 = (g >> 6) & 3, b = (g >> 8) & 1, a = (g >> 9) & 1, gw = g >> 10;
-    const int row = 32 * a + 8 * e4 + 4 * (gl >> 5) + (kYisA ? 0 : 64 * gw);
-    const int col = 32 * b + (gl & 31) + (kYisA ? 64 * gw : 0);
-    if (n0 + col < N) {
+        for (int p = 0; p < kWgMaxSplit; ++p)
+          if (p < ksplit)
+            v += f32x4{__uint_as_float(w[p][0]), __uint_as_float(w[p][1]), __uint_as_float(w[p][2]),
+                       __uint_as_float(w[p][3])};
+        const int gl = g & 63, e4 = (g >> 6) & 3, b = (g >> 8) & 1, a = (g >> 9) & 1, gw = g >> 10;
+        const int row = 32 * a + 8 * e4 + 4 * (gl >> 5) + (kYisA ? 0 : 64 * gw);
+        const int col = 32 * b + (gl & 31) + (kYisA ? 64 * gw : 0);
+        if (n0 + col < N) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (m0 + row + u < M) C[(m0 + row + u) * N + n0 + col] = scale * v[u];
+          for (int u = 0; u < 4; ++u)
+            if (m0 + row + u < M) C[(m0 + row + u) * N + n0 + col] = scale * v[u];
+        }
+      }
     }
+  };
+  const uint32_t mine = claim_lds[0];
+  const bool last = claim_lds[1] != 0u;
+  sum_shares(mine);
+  if (last) {
+    wait_barrier<0>();  // every wave has read the claim words
+    if (wave == 0) {
+      const uint32_t m = split_sweep(line, part, ksplit, lane);
+      if (lane == 0) claim_lds[0] = m;
+    }
+    wait_barrier<0>();
+    sum_shares(claim_lds[0]);
   }
-  wait_vmem();
-  if (tid == 0 && add_dev_u32(tile_counter(counters, tile), 1u) == (uint32_t)(2 * ksplit - 1)) st_dev_u32(tile_counter(counters, tile), 0u);
+  if (tid == 0) split_depart(line, ksplit);
 }
 
 // Token split: as many ranges as keep all of a launch's workgroups resident at
-// once (the ranges of a tile wait for each other), at least two 64-token steps
-// each.
+// once (then the ranges of a tile share the combine), at least two 64-token
+// steps each.
 int lora_wgrad_ksplit(int64_t D, int64_t R, int64_t T) {
   int cus = 256;
   int dev = 0;
@@ -515,7 +529,7 @@ size_t lora_wgrad_partial_floats(int64_t D, int64_t R, int64_t T) {
 static bool g_wg_attr[64];
 
 hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64_t D, int64_t R, bool y_is_rows,
-                             float scale, float *C, float *partial, uint32_t *counters, uint32_t *err,
+                             float scale, float *C, float *partial, uint32_t *counters, uint32_t *fallbacks,
                              hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -532,9 +546,9 @@ hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64
   const int64_t tiles = ((D + kWgD - 1) / kWgD) * ((R + kWgR - 1) / kWgR);
   const dim3 grid((unsigned)tiles, (unsigned)ks);
   if (y_is_rows)
-    k_lora_wgrad<true><<<grid, dim3(256), kWgLds, st>>>(X, Y, T, D, R, scale, C, partial, counters, err, ks);
+    k_lora_wgrad<true><<<grid, dim3(256), kWgLds, st>>>(X, Y, T, D, R, scale, C, partial, counters, fallbacks, ks);
   else
-    k_lora_wgrad<false><<<grid, dim3(256), kWgLds, st>>>(X, Y, T, D, R, scale, C, partial, counters, err, ks);
+    k_lora_wgrad<false><<<grid, dim3(256), kWgLds, st>>>(X, Y, T, D, R, scale, C, partial, counters, fallbacks, ks);
   return hipGetLastError();
 }
 

@@ -10,7 +10,17 @@ the HIP library through the C-ABI binding; this file only marshals tensors.
 
 The forward saves u = x A^T (T x r float32) for the backward's dB, so u is not
 recomputed; with recompute_u the layer keeps only x and the backward forms u
-again (T x r float32 less memory per layer, one more pass over x). With a frozen A (LoRA-FA: "8GB, 12GB, 16GB, 24GB GPU에서 몇 B
+again (T x r float32 less memory per layer, one more pass over x).
+
+The library returns dA and dB in float32. Autograd hands the parameters their
+gradients in the parameters' dtype (bf16), so the layers also keep the float32
+gradients on each adapter parameter, as `param.grad_fp32` (summed over
+backward passes while `param.grad` accumulates, started afresh when
+`param.grad` is None); PagedAdamW steps on those.
+
+The modules compute in bf16 only: a dtype cast of a module (`.to(dtype)`,
+`.half()`, `.float()`) leaves its quantized buffers and adapter parameters as
+they are, and only a device move applies to them. With a frozen A (LoRA-FA: "8GB, 12GB, 16GB, 24GB GPU에서 몇 B
 모델까지 LoRA 학습이 될까", section "LoRA 변형을 바꿔도 답이 같은 이유" -- the
 layer input is not kept) the input x is not saved either: dX needs only dY,
 and dB only u.
@@ -27,12 +37,12 @@ class QLoRALinearFunction(torch.autograd.Function):
     """x [T, d_in] bf16, A [r, d_in] bf16, B [d_out, r] bf16 -> h [T, d_out] bf16."""
 
     @staticmethod
-    def forward(ctx, x, A, B, w: q.NF4Weight, alpha: float, recompute_u: bool = False):
+    def forward(ctx, x, A, B, w: q.NF4Weight, alpha: float, recompute_u: bool = False, grad_sink=None):
         r = 0 if A is None else A.shape[0]
         keep_u = r > 0 and not recompute_u
         h, u = q.qlora_forward(w, x, A, B, alpha, save_u=keep_u)
         keep_x = A is not None and (A.requires_grad or not keep_u)
-        ctx.w, ctx.alpha, ctx.r = w, alpha, r
+        ctx.w, ctx.alpha, ctx.r, ctx.grad_sink = w, alpha, r, grad_sink
         ctx.save_for_backward(x if keep_x else None, A, B, u)
         return h
 
@@ -44,11 +54,40 @@ class QLoRALinearFunction(torch.autograd.Function):
         need_dB = ctx.r > 0 and ctx.needs_input_grad[2]
         dX, dA, dB = q.qlora_backward(ctx.w, x, dh.contiguous(), A, B, ctx.alpha, u_saved=u, need_dx=need_dx,
                                       need_dA=need_dA, need_dB=need_dB)
+        if ctx.grad_sink is not None:
+            ctx.grad_sink(dA, dB)  # the float32 gradients, for the optimizer
         # dA, dB come back in float32 (the library's gradient precision); autograd wants the parameters' dtype
-        return (dX, None if dA is None else dA.to(A.dtype), None if dB is None else dB.to(B.dtype), None, None, None)
+        return (dX, None if dA is None else dA.to(A.dtype), None if dB is None else dB.to(B.dtype), None, None, None,
+                None)
 
 
-class QLoRALinear(torch.nn.Module):
+def _deposit_fp32(p: torch.nn.Parameter, g: torch.Tensor):
+    """Keep the float32 gradient beside p.grad: summed while p.grad accumulates, restarted when it is None."""
+    prev = getattr(p, "grad_fp32", None)
+    if p.grad is None or prev is None:
+        p.grad_fp32 = g.detach().clone()
+    else:
+        prev.add_(g)
+
+
+class _Bf16Module(torch.nn.Module):
+    """Dtype casts leave the quantized storage and the bf16 adapters as they are; device moves apply."""
+
+    def _apply(self, fn, recurse=True):
+        def keep_dtype(t):
+            moved = fn(t)
+            return moved if moved.dtype == t.dtype else t.to(moved.device)
+
+        return super()._apply(keep_dtype, recurse)
+
+    @property
+    def w(self) -> q.NF4Weight:
+        """The quantized weight as the library takes it, built from the registered buffers (so it follows
+        device moves and load_state_dict)."""
+        return q.NF4Weight(self.d_w_out, self.d_in, self.codes, self.qscale, self.smax)
+
+
+class QLoRALinear(_Bf16Module):
     """A frozen NF4 + double-quant weight with a trainable LoRA adapter (bf16 A, B).
 
     A is initialised like the pages' adapters (small random values) and B to zero, so that the adapted
@@ -63,12 +102,13 @@ class QLoRALinear(torch.nn.Module):
             raise ValueError("weight must be [d_out, d_in]")
         d_out, d_in = weight.shape
         # double_quant=False keeps the float32 absmax of every block (4.5 bits per weight)
-        self.w = q.qlora_quantize(weight.contiguous(), double_quant=double_quant)
+        w = q.qlora_quantize(weight.contiguous(), double_quant=double_quant)
         # the quantized buffers are frozen state, not parameters
-        self.register_buffer("codes", self.w.codes, persistent=True)
-        self.register_buffer("qscale", self.w.qscale, persistent=True)
-        self.register_buffer("smax", self.w.smax, persistent=True)
+        self.register_buffer("codes", w.codes, persistent=True)
+        self.register_buffer("qscale", w.qscale, persistent=True)
+        self.register_buffer("smax", w.smax, persistent=True)
         self.d_out, self.d_in, self.r, self.alpha = d_out, d_in, r, float(alpha)
+        self.d_w_out = d_out
         self.recompute_u = recompute_u
         if r > 0:
             A = torch.randn(r, d_in, device=weight.device, generator=generator) * 0.02
@@ -77,10 +117,17 @@ class QLoRALinear(torch.nn.Module):
         else:
             self.A = self.B = None
 
+    def _sink(self, dA, dB):
+        if dA is not None:
+            _deposit_fp32(self.A, dA)
+        if dB is not None:
+            _deposit_fp32(self.B, dB)
+
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.d_in).to(torch.bfloat16).contiguous()
-        h = QLoRALinearFunction.apply(x2, self.A, self.B, self.w, self.alpha, self.recompute_u)
+        h = QLoRALinearFunction.apply(x2, self.A, self.B, self.w, self.alpha, self.recompute_u,
+                                      self._sink if self.r > 0 else None)
         return h.reshape(*lead, self.d_out)
 
     @torch.no_grad()
@@ -89,7 +136,7 @@ class QLoRALinear(torch.nn.Module):
         return q.qlora_merge(self.w, self.A, self.B, self.alpha)
 
 
-class QLoRAFusedLinear(torch.nn.Module):
+class QLoRAFusedLinear(_Bf16Module):
     """Several projections of one input (q/k/v, or gate/up) as one quantized weight and one call.
 
     The weights are stacked along d_out and quantized as one matrix, so every forward reads x once and streams all
@@ -121,10 +168,11 @@ class QLoRAFusedLinear(torch.nn.Module):
         n_ad = sum(self.adapted) if r > 0 else 0
         if n_ad * r > q.MAX_RANK:
             raise ValueError(f"{n_ad} adapters of rank {r} exceed the library's rank limit {q.MAX_RANK}")
-        self.w = q.qlora_quantize(torch.cat(weights, 0), double_quant=double_quant)
-        self.register_buffer("codes", self.w.codes, persistent=True)
-        self.register_buffer("qscale", self.w.qscale, persistent=True)
-        self.register_buffer("smax", self.w.smax, persistent=True)
+        w = q.qlora_quantize(torch.cat(weights, 0), double_quant=double_quant)
+        self.register_buffer("codes", w.codes, persistent=True)
+        self.register_buffer("qscale", w.qscale, persistent=True)
+        self.register_buffer("smax", w.smax, persistent=True)
+        self.d_w_out = sum(self.d_outs)
         self.A = torch.nn.ParameterList()
         self.B = torch.nn.ParameterList()
         dev = weights[0].device
@@ -150,6 +198,20 @@ class QLoRAFusedLinear(torch.nn.Module):
                 parts.append(torch.zeros(d_out, cols, dtype=torch.bfloat16, device=A.device))
         return A, torch.cat(parts, 0)
 
+    def _sink(self, dA, dB):
+        """Split the stacked float32 gradients into the adapters' own (rows of A; B's block on its projection's
+        rows and its adapter's columns)."""
+        row0, k = 0, 0
+        for d_out, ad in zip(self.d_outs, self.adapted):
+            if ad and self.r > 0:
+                cols = slice(k * self.r, (k + 1) * self.r)
+                if dA is not None:
+                    _deposit_fp32(self.A[k], dA[cols])
+                if dB is not None:
+                    _deposit_fp32(self.B[k], dB[row0:row0 + d_out, cols])
+                k += 1
+            row0 += d_out
+
     def forward(self, x: torch.Tensor):
         """Returns one output per projection, [..., d_out_i] each (views of the single call's output)."""
         lead = x.shape[:-1]
@@ -157,5 +219,5 @@ class QLoRAFusedLinear(torch.nn.Module):
         A, B = self.stacked_adapter()
         n_ad = len(self.A)
         alpha = self.alpha * n_ad if n_ad else self.alpha  # scale alpha / (n_ad r) = self.alpha / r
-        h = QLoRALinearFunction.apply(x2, A, B, self.w, alpha, False)
+        h = QLoRALinearFunction.apply(x2, A, B, self.w, alpha, False, self._sink if n_ad else None)
         return tuple(t.reshape(*lead, t.shape[-1]) for t in torch.split(h, self.d_outs, dim=1))

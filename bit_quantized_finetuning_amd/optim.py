@@ -6,6 +6,15 @@ stream. Here each bf16 parameter keeps a float32 master copy in device memory, a
 in pinned host memory (or in device memory with paged=False). One `qlora_adamw_step` per parameter updates them
 in place and rewrites the bf16 parameter; the kernel reads and writes the host-side state over the host link.
 Argument marshalling only: the arithmetic is the library's.
+
+The page has the CPU run the update; here a GPU kernel runs it on a side stream, reading and writing the state in
+pinned host memory in place (the same memory placement, with the arithmetic where the gradients already are, so
+no gradient or state page has to be copied for the CPU to see it).
+
+Gradients: the QLoRA layers keep the library's float32 dA and dB on each adapter parameter as `grad_fp32`
+(autograd's own `.grad` is bf16, the parameters' dtype); the step uses those when present and `.grad` otherwise.
+Zero gradients with `zero_grad()` here (or torch's default set_to_none): the float32 copy restarts whenever
+`.grad` is None.
 """
 
 from __future__ import annotations
@@ -50,6 +59,7 @@ class PagedAdamW:
     def zero_grad(self):
         for p in self.params:
             p.grad = None
+            p.grad_fp32 = None
 
     @torch.no_grad()
     def step(self):
@@ -57,8 +67,13 @@ class PagedAdamW:
         cur = torch.cuda.current_stream(self.params[0].device)
         grads = []
         for p in self.params:
-            # float32 gradient (the layer returns the parameters' dtype), made on the current stream
-            grads.append(None if p.grad is None else p.grad.detach().float().reshape(-1).contiguous())
+            if p.grad is None:
+                grads.append(None)
+                continue
+            g32 = getattr(p, "grad_fp32", None)
+            # the layers' float32 gradient when they left one, else autograd's (bf16) one widened
+            g = g32 if g32 is not None else p.grad.detach().float()
+            grads.append(g.reshape(-1).contiguous())
         ready = torch.cuda.Event()
         ready.record(cur)
         self.stream.wait_event(ready)

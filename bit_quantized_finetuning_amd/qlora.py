@@ -7,8 +7,12 @@ there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
     qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_backward,
-    qlora_adamw_step, qlora_storage_bytes, qlora_storage_bytes_absmax, qlora_workspace_bytes, qlora_nf4_codebook,
-    qlora_nf4_thresholds, qlora_status_string
+    qlora_adamw_step, qlora_workspace_fallbacks, qlora_storage_bytes, qlora_storage_bytes_absmax,
+    qlora_workspace_bytes, qlora_nf4_codebook, qlora_nf4_thresholds, qlora_status_string
+
+The C ABI sees only pointers, so every tensor argument is checked here before the call: its shape against the
+weight and the other operands, its dtype, contiguity, and that it lives on the weight's GPU. A mismatch raises
+TypeError (dtype) or ValueError (shape, layout, device) and nothing is launched.
 """
 
 from __future__ import annotations
@@ -23,8 +27,8 @@ BLOCK = 64
 GROUP = 256
 MAX_RANK = 256
 # The workspace starts with a counter region (u32 words) that must be zero before
-# the first call and that every call leaves zero; its last word is set only if a
-# bounded wait of the skinny-token forward timed out.
+# the first call and that every call leaves zero, except its last word, which
+# counts the waits that ran out of time (qlora_workspace_fallbacks).
 COUNTER_BYTES = 16384 * 4
 
 F32, BF16 = 0, 1
@@ -56,6 +60,8 @@ _lib.qlora_adamw_step.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _vp, _v
 _lib.qlora_adamw_step.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
+_lib.qlora_workspace_fallbacks.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
+_lib.qlora_workspace_fallbacks.restype = ctypes.c_int
 _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_backward.restype = ctypes.c_int
 _lib.qlora_storage_bytes.argtypes = [_i64, _i64]
@@ -199,6 +205,58 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
+def _arg(t, name: str, dtype, shape):
+    """dtype, shape and contiguity of one tensor argument (None passes)."""
+    if t is None:
+        return
+    if not torch.is_tensor(t):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_weight(w: "NF4Weight"):
+    n = w.d_out * w.d_in
+    if w.d_in % BLOCK or n <= 0:
+        raise ValueError(f"weight shape {w.d_out}x{w.d_in}: d_in must be a positive multiple of {BLOCK}")
+    nb = n // BLOCK
+    _arg(w.codes, "codes", torch.uint8, (n // 2,))
+    if w.qscale is not None:
+        _arg(w.qscale, "qscale", torch.uint8, (nb,))
+        _arg(w.smax, "smax", torch.float32, ((nb + GROUP - 1) // GROUP,))
+    else:
+        _arg(w.smax, "smax", torch.float32, (nb,))
+
+
+def _check_devices(device, **tensors):
+    """Every given tensor on `device`, a GPU (the checks that come last, so that the shape rules can be
+    exercised without one)."""
+    if device.type != "cuda":
+        raise ValueError(f"the weight must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the weight on {device}")
+
+
+def _adapter_rank(w: "NF4Weight", A, B) -> int:
+    if (A is None) != (B is None):
+        raise ValueError("give both A and B, or neither")
+    if A is None:
+        return 0
+    if A.dim() != 2:
+        raise ValueError(f"A must be [r, d_in], got shape {tuple(A.shape)}")
+    r = A.shape[0]
+    if r < 0 or r > MAX_RANK or r % 8:
+        raise ValueError(f"rank {r} outside 0..{MAX_RANK} or not a multiple of 8")
+    _arg(A, "A", torch.bfloat16, (r, w.d_in))
+    _arg(B, "B", torch.bfloat16, (w.d_out, r))
+    return r
+
+
 def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.Tensor | None = None,
                    double_quant: bool = True) -> NF4Weight:
     """NF4-quantize W; double_quant=False keeps each block's float32 absmax (ignored when `out` is given)."""
@@ -213,12 +271,22 @@ def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.T
     d_out, d_in = W.shape
     if out is None:
         out = NF4Weight.empty(d_out, d_in, W.device, double_quant)
+    if (out.d_out, out.d_in) != (d_out, d_in):
+        raise ValueError(f"out is {out.d_out}x{out.d_in}, W is {d_out}x{d_in}")
+    _check_weight(out)
+    if flags is not None and (flags.dtype not in (torch.int32, torch.uint32) or flags.numel() < 1):
+        raise TypeError("flags must be a 32-bit integer tensor of at least one element")
+    _check_devices(W.device, codes=out.codes, qscale=out.qscale, smax=out.smax, flags=flags)
     cw = out._c()
     _check(_lib.qlora_quantize(_ptr(W), dt, ctypes.byref(cw), _ptr(flags), _stream(W.device)), "qlora_quantize")
     return out
 
 
 def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"dtype must be bfloat16 or float32, got {dtype}")
+    _check_weight(w)
+    _check_devices(w.codes.device, qscale=w.qscale, smax=w.smax)
     out = torch.empty(w.d_out, w.d_in, dtype=dtype, device=w.codes.device)
     dt = BF16 if dtype == torch.bfloat16 else F32
     cw = w._c()
@@ -229,11 +297,13 @@ def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:
 def qlora_merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
                 out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 [d_out, d_in] = bf16(W_hat + (alpha/r) B A): the adapter merged into the restored weight."""
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _bits(A), _bits(B)
+    _check_weight(w)
+    r = _adapter_rank(w, A, B)
+    _arg(out, "out", torch.bfloat16, (w.d_out, w.d_in))
+    dev = w.codes.device
+    _check_devices(dev, qscale=w.qscale, smax=w.smax, A=A, B=B, out=out)
     if out is None:
-        out = torch.empty(w.d_out, w.d_in, dtype=torch.bfloat16, device=w.codes.device)
+        out = torch.empty(w.d_out, w.d_in, dtype=torch.bfloat16, device=dev)
     cw = w._c()
     _check(_lib.qlora_merge(ctypes.byref(cw), _ptr(A), _ptr(B), r, alpha, _ptr(out), _stream(out.device)),
            "qlora_merge")
@@ -259,10 +329,38 @@ def qlora_adamw_step(step: int, grad: torch.Tensor, master: torch.Tensor, m: tor
         raise ValueError("all tensors must have the same number of elements")
     if param is not None:
         _bits(param)
+    if grad.device.type != "cuda":
+        raise ValueError(f"grad must be on a GPU, got {grad.device}")
+    _check_devices(grad.device, param=param)
+    for name, t in (("master", master), ("m", m), ("v", v)):
+        if t.device != grad.device and not (t.device.type == "cpu" and t.is_pinned()):
+            raise ValueError(f"{name} must be on the gradient's GPU or in pinned host memory, got {t.device}")
     hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay)
     st = ctypes.c_void_p((stream or torch.cuda.current_stream(grad.device)).cuda_stream)
     _check(_lib.qlora_adamw_step(ctypes.byref(hp), step, n, _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
                                  _ptr(param), st), "qlora_adamw_step")
+
+
+def _forward_args(w, x, A, B, h, u, save_u, ws=None):
+    _check_weight(w)
+    if not torch.is_tensor(x) or x.dim() != 2:
+        raise ValueError("x must be a 2-D [T, d_in] tensor")
+    T = x.shape[0]
+    _arg(x, "x", torch.bfloat16, (T, w.d_in))
+    r = _adapter_rank(w, A, B)
+    _arg(h, "h", torch.bfloat16, (T, w.d_out))
+    if u is not None and r == 0:
+        raise ValueError("u is given but there is no adapter")
+    _arg(u, "u", torch.float32, (T, r))
+    if ws is not None:
+        _own_workspace(ws, qlora_workspace_bytes(w.d_out, w.d_in, T, r))
+    dev = w.codes.device
+    _check_devices(dev, qscale=w.qscale, smax=w.smax, x=x, A=A, B=B, h=h, u=u, ws=ws)
+    if h is None:
+        h = torch.empty(T, w.d_out, dtype=torch.bfloat16, device=dev)
+    if u is None and save_u and r > 0:
+        u = torch.empty(T, r, dtype=torch.float32, device=dev)
+    return T, r, h, u
 
 
 def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, alpha: float,
@@ -272,21 +370,23 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
 
     h and u may be passed in (preallocated outputs); otherwise they are allocated here.
     """
-    x = _bits(x)
-    T = x.shape[0]
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _bits(A), _bits(B)
-    if h is None:
-        h = torch.empty(T, w.d_out, dtype=torch.bfloat16, device=x.device)
-    if u is None and save_u and r > 0:
-        u = torch.empty(T, r, dtype=torch.float32, device=x.device)
-    nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
-    ws = workspace(x.device, nbytes) if ws is None else _own_workspace(ws, nbytes)
+    T, r, h, u = _forward_args(w, x, A, B, h, u, save_u, ws)
+    if ws is None:
+        ws = workspace(x.device, qlora_workspace_bytes(w.d_out, w.d_in, T, r))
     cw = w._c()
     _check(_lib.qlora_forward(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
                               _ptr(ws), ws.numel(), _stream(x.device)), "qlora_forward")
     return h, u
+
+
+def qlora_workspace_fallbacks(ws: torch.Tensor) -> int:
+    """How many waits on this workspace ran out of time and took their fallback path (the results are the same;
+    a nonzero count means launches on other streams held the compute units). Synchronizes the current stream."""
+    _own_workspace(ws, COUNTER_BYTES)
+    _check_devices(ws.device)
+    n = ctypes.c_uint32(0)
+    _check(_lib.qlora_workspace_fallbacks(_ptr(ws), ctypes.byref(n), _stream(ws.device)), "qlora_workspace_fallbacks")
+    return int(n.value)
 
 
 def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor | None,
@@ -298,18 +398,32 @@ def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: to
 
     Outputs passed in are written in place (and count as needed); the others are allocated when needed.
     """
-    dY = _bits(dY)
+    _check_weight(w)
+    if not torch.is_tensor(dY) or dY.dim() != 2:
+        raise ValueError("dY must be a 2-D [T, d_out] tensor")
     T = dY.shape[0]
-    r = 0 if A is None else A.shape[0]
-    dev = dY.device
+    _arg(dY, "dY", torch.bfloat16, (T, w.d_out))
+    _arg(x, "x", torch.bfloat16, (T, w.d_in))
+    r = _adapter_rank(w, A, B)
+    if r == 0 and (dA is not None or dB is not None or u_saved is not None):
+        raise ValueError("dA, dB and u_saved need an adapter")
+    _arg(u_saved, "u_saved", torch.float32, (T, r))
+    _arg(dX, "dX", torch.bfloat16, (T, w.d_in))
+    _arg(dA, "dA", torch.float32, (r, w.d_in))
+    _arg(dB, "dB", torch.float32, (w.d_out, r))
+    nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
+    if ws is not None:
+        _own_workspace(ws, nbytes)
+    dev = w.codes.device
+    _check_devices(dev, qscale=w.qscale, smax=w.smax, x=x, dY=dY, A=A, B=B, u_saved=u_saved, dX=dX, dA=dA, dB=dB,
+                   ws=ws)
     if dX is None and need_dx:
         dX = torch.empty(T, w.d_in, dtype=torch.bfloat16, device=dev)
     if dA is None and need_dA and r > 0:
         dA = torch.empty(r, w.d_in, dtype=torch.float32, device=dev)
     if dB is None and need_dB and r > 0:
         dB = torch.empty(w.d_out, r, dtype=torch.float32, device=dev)
-    nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
-    ws = workspace(dev, nbytes) if ws is None else _own_workspace(ws, nbytes)
+    ws = workspace(dev, nbytes) if ws is None else ws
     cw = w._c()
     _check(_lib.qlora_backward(ctypes.byref(cw), _ptr(x), _ptr(dY), T, _ptr(A), _ptr(B), r, alpha, _ptr(u_saved),
                                _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)), "qlora_backward")

@@ -27,7 +27,11 @@
  *     1 <= T <= QLORA_MAX_TOKENS; 0 <= r <= 256 with r % 8 == 0.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Calls that run concurrently (other streams or threads) must not share a
- *     workspace.
+ *     workspace; with distinct workspaces they may overlap freely. No kernel
+ *     depends on another launch finishing, or on all of its own workgroups
+ *     being resident at once: where workgroups of one launch wait for each
+ *     other, a wait that runs out of time (about 200 us) takes a path that
+ *     needs no one else and gives the same bits (see qlora_workspace_fallbacks).
  *   - The header is plain C: it needs only hip_runtime_api.h for hipStream_t.
  *     A host compiler other than hipcc defines __HIP_PLATFORM_AMD__ for that
  *     header, as `hipconfig --cpp_config` prints.
@@ -145,9 +149,9 @@ int qlora_merge(const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B,
  *   ws     device workspace of at least qlora_workspace_bytes(d_out, d_in, T, r)
  *          bytes. Its first QLORA_WS_COUNTER_BYTES bytes are u32 counters that
  *          must be zero before the first use of the workspace; every call leaves
- *          them zero again. The last of them becomes nonzero only if a bounded
- *          wait in the T <= 16 kernel timed out (the call's output is then
- *          unspecified). The rest of the workspace needs no initialisation.
+ *          them zero again, except the last one, which counts the waits that ran
+ *          out of time (qlora_workspace_fallbacks; the output never depends on
+ *          it). The rest of the workspace needs no initialisation.
  * T <= 16 runs one weight-streaming kernel (the adapter intermediate is formed
  * by the last workgroups of the same launch); larger T runs the MFMA GEMM.
  */
@@ -204,6 +208,15 @@ typedef struct {
 
 int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, const float *grad, float *master,
                      float *m, float *v, uint16_t *param, hipStream_t stream);
+
+/*
+ * Host: the number of waits that ran out of time on this workspace since it
+ * was zeroed (the last u32 of its counter region). Such a wait means another
+ * launch held the compute units the awaited workgroups needed; the results are
+ * the same, only slower. Copies one word on `stream` and synchronizes it.
+ * Errors: NULL, HIP.
+ */
+int qlora_workspace_fallbacks(const void *ws, uint32_t *count, hipStream_t stream);
 
 /* Bytes of the quantized weight: n/2 + n/64 + 4*ceil(n/16384). */
 size_t qlora_storage_bytes(int64_t d_out, int64_t d_in);

@@ -19,6 +19,26 @@ import torch
 import oracle
 from bit_quantized_finetuning_amd import synth
 
+def product(name: str):
+    """A module of the package for a GPU test module: the module itself, or (when it does not import, e.g. the
+    library is not built) a stand-in whose every use fails the test loudly. Collection of the GPU test modules
+    thus never depends on the library, and a GPU run without it fails instead of skipping."""
+    import importlib
+
+    try:
+        return importlib.import_module(f"bit_quantized_finetuning_amd.{name}")
+    except ImportError as e:  # pragma: no cover - exercised only without the library
+        err = e
+
+        class _Missing:
+            def __getattr__(self, attr):
+                import pytest
+
+                pytest.fail(f"bit_quantized_finetuning_amd.{name} does not import: {err}")
+
+        return _Missing()
+
+
 REL_FRO = 5e-3
 MAX_ABS = 1e-2
 

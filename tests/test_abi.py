@@ -13,7 +13,11 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
 
-q = pytest.importorskip("bit_quantized_finetuning_amd.qlora", reason="libqlora.so not built")
+from bit_quantized_finetuning_amd import build as _build  # noqa: E402
+
+if not os.path.exists(_build.LIB):  # hipcc cross-compiles for gfx950 without a GPU
+    _build.build()
+from bit_quantized_finetuning_amd import qlora as q  # noqa: E402
 
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_DTYPE = -1, -2, -3, -4, -5
 

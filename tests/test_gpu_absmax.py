@@ -15,12 +15,12 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import Case, assert_close, assert_within_one_bf16_ulp, merge_float32_slack, say
+from gpu_common import Case, assert_close, assert_within_one_bf16_ulp, merge_float32_slack, say, product
 
 pytestmark = pytest.mark.gpu
 
-q = pytest.importorskip("bit_quantized_finetuning_amd.qlora")
-layer = pytest.importorskip("bit_quantized_finetuning_amd.layer")
+q = product("qlora")
+layer = product("layer")
 
 
 class AbsmaxCase(Case):

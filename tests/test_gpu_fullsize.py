@@ -17,11 +17,11 @@ import torch
 
 import oracle
 from bit_quantized_finetuning_amd import synth
-from gpu_common import assert_close, assert_within_one_bf16_ulp, bits_to_bf16, merge_float32_slack, say
+from gpu_common import assert_close, assert_within_one_bf16_ulp, bits_to_bf16, merge_float32_slack, say, product
 
 pytestmark = pytest.mark.gpu
 
-q = pytest.importorskip("bit_quantized_finetuning_amd.qlora")
+q = product("qlora")
 
 NSAMP = 64
 

@@ -7,11 +7,11 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import Case, assert_close, bits_to_bf16, say
+from gpu_common import Case, assert_close, bits_to_bf16, say, product
 
 pytestmark = pytest.mark.gpu
 
-layer = pytest.importorskip("bit_quantized_finetuning_amd.layer")
+layer = product("layer")
 
 
 def _module(case, freeze_A=False):
@@ -125,6 +125,13 @@ def test_fused_qkv_matches_separate_projections(T):
             k = 0 if i == 0 else 1
             assert_close(f"dA[{i}]", m.A[k].grad, dA_i)
             assert_close(f"dB[{i}]", m.B[k].grad, dB_i)
+            # the float32 gradients kept for the optimizer: the stacked call's blocks of this adapter, of which
+            # autograd's bf16 gradients are the rounding
+            assert_close(f"dA32[{i}]", m.A[k].grad_fp32, dA_i)
+            assert_close(f"dB32[{i}]", m.B[k].grad_fp32, dB_i)
+            for p in (m.A[k], m.B[k]):
+                assert p.grad_fp32.dtype == torch.float32 and p.grad_fp32.shape == p.shape
+                assert torch.equal(p.grad_fp32.to(torch.bfloat16).view(torch.int16), p.grad.view(torch.int16))
     assert_close("dX", x.grad, dX_ref)
 
 
@@ -206,3 +213,30 @@ def test_recompute_u_keeps_no_intermediate(T):
         assert_close(f"dX rec={rec}", grads[rec][0], dX_ref)
         assert_close(f"dA rec={rec}", grads[rec][1], dA_ref)
         assert_close(f"dB rec={rec}", grads[rec][2], dB_ref)
+
+
+def test_state_dict_round_trip_after_dtype_cast():
+    """A dtype cast leaves the quantized buffers (float32 group maxima included) and the bf16 adapters as they
+    are; state_dict then reloads into a fresh module bit for bit, and the reloaded module computes from the
+    loaded buffers (its output equals the original's)."""
+    say("state_dict after .to(bfloat16)")
+    torch.manual_seed(5)
+    W = (torch.randn(256, 320) * 0.02).cuda()
+    m = layer.QLoRALinear(W, r=8, alpha=16.0)
+    with torch.no_grad():
+        m.B.copy_((torch.randn(256, 8) * 0.02).to(torch.bfloat16))
+    smax0 = m.smax.clone()
+    m.to(torch.bfloat16)
+    m.half()
+    assert m.smax.dtype == torch.float32 and torch.equal(m.smax.view(torch.int32), smax0.view(torch.int32))
+    assert m.A.dtype == torch.bfloat16 and m.B.dtype == torch.bfloat16
+    sd = m.state_dict()
+    W2 = (torch.randn(256, 320) * 0.02).cuda()  # another weight: every buffer differs until loaded
+    m2 = layer.QLoRALinear(W2, r=8, alpha=16.0)
+    m2.load_state_dict(sd)
+    for k in ("codes", "qscale", "smax", "A", "B"):
+        a, b = getattr(m, k), getattr(m2, k)
+        assert a.dtype == b.dtype and torch.equal(a.view(torch.uint8), b.view(torch.uint8)), k
+    x = torch.randn(16, 320).to(torch.bfloat16).cuda()
+    with torch.no_grad():
+        assert torch.equal(m(x).view(torch.int16), m2(x).view(torch.int16))

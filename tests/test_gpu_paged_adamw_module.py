@@ -1,18 +1,18 @@
 """PagedAdamW on a QLoRALinear (needs an MI355X): three training steps (forward, backward, update on a side
-stream) against the float64 AdamW oracle run on the same gradients; state paged to pinned host memory and kept
-on the device."""
+stream) against the float64 AdamW oracle run on the same float32 gradients; state paged to pinned host memory and
+kept on the device."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_common import say
+from gpu_common import say, product
 
 pytestmark = pytest.mark.gpu
 
-layer = pytest.importorskip("bit_quantized_finetuning_amd.layer")
-optim = pytest.importorskip("bit_quantized_finetuning_amd.optim")
+layer = product("layer")
+optim = product("optim")
 
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
@@ -38,7 +38,11 @@ def test_paged_adamw_trains_a_layer_like_the_oracle(paged):
         opt.zero_grad()
         loss = ((m(x).float() - target) ** 2).mean()
         loss.backward()
-        grads = [p.grad.detach().float().cpu().numpy().astype(np.float64).reshape(-1) for p in opt.params]
+        # the optimizer steps on the library's float32 gradients, kept beside autograd's bf16 ones
+        for p in opt.params:
+            assert p.grad_fp32.dtype == torch.float32
+            assert torch.equal(p.grad_fp32.to(torch.bfloat16).view(torch.int16), p.grad.view(torch.int16))
+        grads = [p.grad_fp32.detach().cpu().numpy().astype(np.float64).reshape(-1) for p in opt.params]
         opt.step()
         for k, (st, g) in enumerate(zip(ref, grads)):
             st[0], st[1], st[2] = oracle.adamw_step(st[0], st[1], st[2], g, step, **HP)
