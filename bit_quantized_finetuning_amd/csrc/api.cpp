@@ -249,6 +249,7 @@ const char *qlora_status_string(int status) {
     case QLORA_ERR_INTERNAL: return "internal: the kernels' NF4 levels differ from the derived table";
     case QLORA_ERR_MEMORY: return "a pointer is neither device memory nor pinned host memory";
     case QLORA_ERR_VALUE: return "a hyperparameter is out of range (or step < 1)";
+    case QLORA_ERR_SCRATCH: return "qlora_forward_noalloc takes T <= 16 only (its static scratch array holds that path)";
     default: return "unknown status";
   }
 }

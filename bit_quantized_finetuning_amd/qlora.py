@@ -6,7 +6,7 @@ allocates nothing. If the library is missing this module raises at import --
 there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
-    qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_backward,
+    qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_forward_noalloc, qlora_backward,
     qlora_adamw_step, qlora_workspace_fallbacks, qlora_storage_bytes, qlora_storage_bytes_absmax,
     qlora_workspace_bytes, qlora_nf4_codebook, qlora_nf4_thresholds, qlora_status_string
 
@@ -30,6 +30,7 @@ MAX_RANK = 256
 # the first call and that every call leaves zero, except its last word, which
 # counts the waits that ran out of time (qlora_workspace_fallbacks).
 COUNTER_BYTES = 16384 * 4
+STATIC_SCRATCH_BYTES = 1 << 20  # QLORA_STATIC_SCRATCH_BYTES: scratch of qlora_forward_noalloc per GPU
 
 F32, BF16 = 0, 1
 
@@ -60,6 +61,8 @@ _lib.qlora_adamw_step.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _vp, _v
 _lib.qlora_adamw_step.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
+_lib.qlora_forward_noalloc.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp]
+_lib.qlora_forward_noalloc.restype = ctypes.c_int
 _lib.qlora_workspace_fallbacks.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
 _lib.qlora_workspace_fallbacks.restype = ctypes.c_int
 _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -376,6 +379,20 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
     cw = w._c()
     _check(_lib.qlora_forward(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
                               _ptr(ws), ws.numel(), _stream(x.device)), "qlora_forward")
+    return h, u
+
+
+def qlora_forward_noalloc(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+                          alpha: float, h: torch.Tensor, u: torch.Tensor | None = None):
+    """qlora_forward for T <= 16 on the library's static per-GPU scratch array instead of a workspace: no
+    allocation in the library or here (h, and u when wanted, are the caller's). Calls that overlap on one GPU
+    share the array and must be serialized by the caller."""
+    if h is None:
+        raise ValueError("qlora_forward_noalloc writes into a given h (it allocates nothing)")
+    T, r, h, u = _forward_args(w, x, A, B, h, u, False)
+    cw = w._c()
+    _check(_lib.qlora_forward_noalloc(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
+                                      _stream(x.device)), "qlora_forward_noalloc")
     return h, u
 
 

@@ -53,6 +53,7 @@ extern "C" {
 #define QLORA_MAX_DIM (1 << 20)          /* d_in, d_out upper bound            */
 #define QLORA_MAX_TOKENS (1 << 24)       /* T upper bound                      */
 #define QLORA_WS_COUNTER_BYTES 65536     /* zeroed counter region of a workspace */
+#define QLORA_STATIC_SCRATCH_BYTES (1u << 20) /* scratch of qlora_forward_noalloc per GPU */
 
 typedef enum {
   QLORA_OK = 0,
@@ -66,7 +67,9 @@ typedef enum {
                                the table derived at load (never expected)      */
   QLORA_ERR_MEMORY = -8,    /* a pointer is neither device memory nor pinned
                                (hipHostMalloc) host memory                     */
-  QLORA_ERR_VALUE = -9      /* a hyperparameter is out of range                */
+  QLORA_ERR_VALUE = -9,     /* a hyperparameter is out of range                */
+  QLORA_ERR_SCRATCH = -10   /* qlora_forward_noalloc: T > 16, or more scratch
+                               than QLORA_STATIC_SCRATCH_BYTES                 */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -208,6 +211,26 @@ typedef struct {
 
 int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, const float *grad, float *master,
                      float *m, float *v, uint16_t *param, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qlora_forward without a
+ * workspace argument, for the weight-streaming regime of T <= 16 tokens (the
+ * decode-shaped calls of a serving loop). Its scratch -- the counter region and
+ * the tagged exchange of the adapter intermediate, about 200 KB at r = 256 --
+ * is one static device array of QLORA_STATIC_SCRATCH_BYTES per GPU, held until
+ * the process ends; the library takes its address once per device
+ * (hipGetSymbolAddress) on the first call there and clears it with a fill
+ * kernel on `stream`. Arguments, layouts and results are those of
+ * qlora_forward, bit for bit. The call allocates nothing. Calls that overlap
+ * on one GPU (other streams, other threads) share that array and race:
+ * serialize them. Errors: those of qlora_forward; SCRATCH for T > 16 or a call
+ * the array cannot hold; HIP when the array's address cannot be had. Nothing
+ * is enqueued on an error.
+ */
+int qlora_forward_noalloc(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A,
+                          const uint16_t *B, int32_t r, float alpha, uint16_t *h, float *u_out,
+                          hipStream_t stream);
 
 /*
  * Host: the number of waits that ran out of time on this workspace since it
