@@ -1,47 +1,48 @@
 #!/usr/bin/env python3
 """Benchmark of the QLoRA frozen-NF4 linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_skinny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 65b_layer]
 
-Default workload (LLaMA-7B-shaped projections, the weight-streaming regime):
-4096x4096 and 11008x4096 NF4 + double-quant weights (W ~ N(0, 0.02^2)), LoRA r=64
-alpha=16 (A, B ~ N(0, 0.02^2) bf16), x ~ N(0, 1) bf16 with 1, 4 and 16 tokens.
-One step = the forward h = dequant(W) x + (alpha/r) B A x of both projections at
-all three token counts (6 calls, each one launch of the weight-streaming kernel).
-Quantization happens once before timing, as at model load.
+Default workload (the largest configuration that fits one GPU): one decoder layer of a 65B model, hidden 8192,
+MLP 22016 -- q, k, v, o 8192x8192, gate and up 22016x8192, down 8192x22016 -- every projection an NF4 +
+double-quant weight (W ~ N(0, 0.02^2)) with a LoRA adapter r=64 alpha=16 (A, B ~ N(0, 0.02^2) bf16), at
+batch 8 x seq 512 = 4096 tokens (x, dY ~ N(0, 1) bf16). One step = for every projection the forward
+h = dequant(W) x + (alpha/r) B A x (u saved) and the backward dX, dA, dB. Quantization happens once before
+timing, as at model load.
 
-Timing. The steps are captured into HIP graphs (a chunk of C steps, replayed),
-so that the host's per-call cost does not leave the GPU idle between 8-15 us
-kernels; HIP events on the replay stream bracket exactly K steps. Every call of
-a chunk reads its own copy of the quantized weight and adapters, so between two
-reads of one copy more than 600 MB of other weights stream by and HBM, not the
-256 MB Infinity Cache, serves the weight stream.
+Timing. W warm-up steps, then exactly K steps between HIP events on the launch stream, the region bracketed by
+torch.cuda.synchronize(). Launches are eager (every kernel runs hundreds of microseconds, so the host stays
+ahead), with HIP events on the same stream around every forward and backward call.
 
-Printed: one JSON line. `value` is the weight GB/s (packed codes + scale codes +
-group maxima per second); `roofline` is the weight-streaming kernel's algorithmic
-bytes per launch over its mean launch duration in the timed region; `cpu_baseline`
-is the CPU oracle timed on a bounded sample of the same workload.
+Printed: one JSON line.
+  value       TFLOP/s of the whole step (forward + backward flops of every projection / step time).
+  roofline    the fused dequant-GEMM + LoRA forward call (qlora_forward: k_lora_tall forms u = x A^T, then
+              k_gemm_fwd the tiled contraction with the adapter term as extra K columns): its algorithmic flops
+              over its mean duration, from the events around every forward call in the timed region, against
+              the 2.5 PFLOP/s bf16 dense MFMA peak.
+  cpu_baseline the CPU oracle (float64) on a bounded sample -- row slices of one projection of each distinct
+              shape at a reduced token count -- scaled linearly to the step (flagged "scaled").
+  skinny      the weight-streaming regime on the LLaMA-7B projections (4096x4096 and 11008x4096, r=64, T = 1, 4
+              and 16, forward): weight GB/s and the k_gemv_fwd roofline against 8 TB/s (graph-replayed, each
+              call on its own weight copy so that HBM serves the stream).
+  hbm_ceiling a streaming read and a device copy of 2 GiB measured in the same run (torch kernels).
+  per_call    every forward and backward call's mean duration and TFLOP/s.
 
-Other workloads are records, not the headline line:
-  65b_skinny  the same weight-streaming forward (T = 1, 16; r = 64) on the 65B layer's
-      8192x8192, 22016x8192 and 8192x22016 weights (34-93 MB per call);
-  13b_4096tok / 65b_layer / linear1024 / 14b_stack  the MFMA GEMM regime
-      (forward + backward; 14b_stack: one of the 40 identical layers of the
-      14B-style stack, bf16 source weights, 2048 tokens, LoRA r=8 on q and v);
-  14b_stack_fused  the same layer with q/k/v and gate/up each stacked into one
-      call that reads its input once (q and v adapters as one block-diagonal
-      rank-16 pair);
-  14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack
-      (13.2 G parameters, generated on the device from a seeded generator);
-  merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two
-      LLaMA-7B projections with r = 64;
-  13b_paged_adamw  the 13b_4096tok step, timed without and with an AdamW update
-      of every A and B whose moments m, v sit in pinned host memory (float32
-      master on the device); the update of a projection runs on a side stream
-      beside the next projection's forward and backward. Reported: the step with
-      the update and the throughput lost to it.
-  --storage absmax  any forward/backward workload on absmax-only weights (one
-      float32 scale per 64-weight block, 4.5 bits) instead of double quant.
+Other workloads (--workload) are records, not the headline line:
+  llama7b_skinny / 65b_skinny  the weight-streaming forward alone (T <= 16; graph-replayed);
+  13b_4096tok / linear1024 / 14b_stack  forward + backward of the 13B projections, the single-linear parity
+      config, one of the 40 identical layers of the 14B-style stack (bf16 source weights, 2048 tokens, LoRA
+      r=8 on q and v);
+  14b_stack_fused  the same layer with q/k/v and gate/up each stacked into one call that reads its input once
+      (q and v adapters as one block-diagonal rank-16 pair);
+  14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack (13.2 G parameters, generated
+      on the device from a seeded generator);
+  merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two LLaMA-7B projections with r = 64;
+  13b_paged_adamw  the 13b_4096tok step, timed without and with an AdamW update of every A and B whose moments
+      m, v sit in pinned host memory (float32 master on the device); the update of a projection runs on a side
+      stream beside the next projection's forward and backward.
+  --storage absmax  any forward/backward workload on absmax-only weights (one float32 scale per 64-weight
+      block, 4.5 bits) instead of double quant.
 """
 
 from __future__ import annotations
@@ -68,13 +69,15 @@ WORKLOAD_CHOICES = ["llama7b_skinny", "65b_skinny", "linear1024", "13b_4096tok",
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llama7b_skinny", choices=WORKLOAD_CHOICES)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default: 20, or 200 for T <= 16 workloads)")
+    p.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: 3, or 20 for T <= 16)")
+    p.add_argument("--workload", default="65b_layer", choices=WORKLOAD_CHOICES)
     p.add_argument("--chunk", type=int, default=20, help="steps per captured graph")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-per-call", action="store_true", help="skip the per-call-shape timings (profiling runs)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="default workload: skip the skinny and HBM-ceiling measurements (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--storage", default="dq", choices=["dq", "absmax"],
                    help="weight storage: NF4 with double-quantized scales (4.13 bits) or float32 block absmax (4.5)")
@@ -82,7 +85,13 @@ def parse():
                    help="13b_paged_adamw: update m, v in host memory in place, or copy each page to the device and back")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
-    return p.parse_args()
+    a = p.parse_args()
+    skinny = a.workload in ("llama7b_skinny", "65b_skinny", "merge_llama7b")
+    if a.steps is None:
+        a.steps = 200 if skinny else 20
+    if a.warmup is None:
+        a.warmup = 20 if skinny else 3
+    return a
 
 
 ABSMAX_STORAGE = [False]  # set from --storage
@@ -115,6 +124,9 @@ def bwd_flops(d_out, d_in, r, T):
     return 2 * T * d_in * d_out + 4 * T * r * (d_in + d_out)
 
 
+TRAIN_WORKLOADS = ("65b_layer", "13b_4096tok", "14b_stack", "14b_stack_fused", "linear1024")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -137,8 +149,174 @@ def main():
         return bench_merge(args, torch, q, synth, dev)
     if args.workload == "14b_quantize":
         return bench_quantize_stack(args, torch, q, synth, dev)
-    paged = args.workload == "13b_paged_adamw"
-    wname = "13b_4096tok" if paged else args.workload
+    if args.workload == "13b_paged_adamw":
+        return bench_graph(args, torch, q, synth, dev, "13b_4096tok", paged=True)
+    if args.workload in TRAIN_WORKLOADS:
+        return bench_train(args, torch, q, synth, dev, args.workload)
+    return bench_graph(args, torch, q, synth, dev, args.workload)
+
+
+def bench_train(args, torch, q, synth, dev, wname):
+    """Forward + backward of every projection of a workload, eager launches, HIP events around every call."""
+    wl = synth.WORKLOADS[wname]
+    cfg = synth.WORKLOAD_SEED[wname]
+    (T,) = wl.tokens
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    projs = []
+    for pi, p in enumerate(wl.projections):
+        W = torch.from_numpy(synth.weight(cfg, pi, p.d_out, p.d_in, wl.weight_dtype)).to(dev)
+        w = q.qlora_quantize(W, double_quant=not ABSMAX_STORAGE[0])
+        del W
+        A = B = None
+        if p.r > 0:
+            (_, A_bits), (_, B_bits) = synth.adapters(cfg, pi, p.d_out, p.d_in, p.r)
+            A, B = dev16(A_bits), dev16(B_bits)
+            if p.b_rows:  # stacked projections: block-diagonal B (adapter k on its projection's rows only)
+                mask = torch.zeros_like(B, dtype=torch.bool)
+                rk = p.r // len(p.b_rows)
+                for k, (r0, r1) in enumerate(p.b_rows):
+                    mask[r0:r1, k * rk:(k + 1) * rk] = True
+                B = torch.where(mask, B, torch.zeros_like(B))
+        x = dev16(synth.tokens(cfg, pi, T, p.d_in)[1])
+        dy = dev16(synth.upstream_grad(cfg, pi, T, p.d_out)[1])
+        h = torch.empty(T, p.d_out, dtype=torch.bfloat16, device=dev)
+        u = torch.empty(T, p.r, dtype=torch.float32, device=dev) if p.r > 0 else None
+        dX = torch.empty(T, p.d_in, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(p.r, p.d_in, dtype=torch.float32, device=dev) if p.r > 0 else None
+        dB = torch.empty(p.d_out, p.r, dtype=torch.float32, device=dev) if p.r > 0 else None
+        projs.append((p, w, A, B, x, dy, h, u, dX, dA, dB))
+    ws = q.workspace(dev, max(q.qlora_workspace_bytes(p.d_out, p.d_in, T, p.r) for p in wl.projections))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    n = len(projs)
+
+    def step(ev=None):
+        for i, (p, w, A, B, x, dy, h, u, dX, dA, dB) in enumerate(projs):
+            if ev is not None:
+                ev[2 * i].record(stream)
+            q.qlora_forward(w, x, A, B, p.alpha, h=h, u=u, ws=ws)
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+        for i, (p, w, A, B, x, dy, h, u, dX, dA, dB) in enumerate(reversed(projs)):
+            j = n - 1 - i
+            if ev is not None:
+                ev[2 * n + 2 * j].record(stream)
+            q.qlora_backward(w, x, dy, A, B, p.alpha, u_saved=u, dX=dX, dA=dA, dB=dB, ws=ws)
+            if ev is not None:
+                ev[2 * n + 2 * j + 1].record(stream)
+
+    print(f"[bench] {wname}: inputs ready, {args.warmup} warm-up + {args.steps} timed steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * n)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    fwd_ms = [np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs]) for i in range(n)]
+    bwd_ms = [np.mean([e[2 * n + 2 * i].elapsed_time(e[2 * n + 2 * i + 1]) for e in evs]) for i in range(n)]
+
+    ff = sum(fwd_flops(p.d_out, p.d_in, p.r, T) for p, *_ in projs)
+    bf = sum(bwd_flops(p.d_out, p.d_in, p.r, T) for p, *_ in projs)
+    tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
+    # the fused dequant-GEMM + LoRA forward: algorithmic flops of all forward calls over their summed duration
+    fwd_tf = ff / (sum(fwd_ms) * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(FWD_TRAFFIC_RECORD),
+            "kernel": "qlora_forward at T = %d: k_lora_tall (u = x A^T) then k_gemm_fwd (dequant GEMM with the "
+                      "adapter term as extra K columns)" % T if T >= 65 else "qlora_forward",
+            "flops_per_launch": round(ff / n), "us_per_launch": round(1e3 * sum(fwd_ms) / n, 2),
+            "launches": args.steps * n, "timing": "HIP events around every forward call in the timed region"}
+    per_call = []
+    for i, (p, *_r) in enumerate(projs):
+        for kind, ms, fl in (("fwd", fwd_ms[i], fwd_flops(p.d_out, p.d_in, p.r, T)),
+                             ("bwd", bwd_ms[i], bwd_flops(p.d_out, p.d_in, p.r, T))):
+            per_call.append({"proj": f"{p.name} {p.d_out}x{p.d_in}", "call": kind, "r": p.r,
+                             "us": round(ms * 1e3, 1), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1)})
+    wbytes = 2 * sum(weight_bytes(p.d_out, p.d_in) for p, *_ in projs)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s (forward + backward of every projection)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights and adapters, N(0,1) tokens and upstream gradients)",
+        "config": {"workload": wl.description, "projections": [f"{p.name} {p.d_out}x{p.d_in}" for p in wl.projections],
+                   "tokens": T, "lora_r": [p.r for p in wl.projections], "lora_alpha": wl.projections[0].alpha,
+                   "backward": True, "launch": "eager",
+                   "weight_storage": ("NF4 + float32 absmax per 64-weight block (4.5 bits)" if ABSMAX_STORAGE[0]
+                                      else "NF4 + double-quantized block scales (4.127 bits)"),
+                   **({"layers_in_stack": wl.layers, "layers_per_step": 1} if wl.layers > 1 else {})},
+        "weight_GBs": round(wbytes / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": roof,
+        "per_call": per_call,
+        "workspace_fallbacks": q.qlora_workspace_fallbacks(ws),
+        "cpu_baseline": None,
+    }
+    print(f"[bench] {wname}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_train(args, wl, cfg, ms_step, ff + bf)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+    if wname == "65b_layer" and not args.no_extras:
+        import copy
+
+        del projs
+        torch.cuda.empty_cache()
+        sargs = copy.copy(args)
+        sargs.steps, sargs.warmup, sargs.no_cpu_baseline = 200, 20, True
+        sk = bench_graph(sargs, torch, q, synth, dev, "llama7b_skinny", emit=False)
+        line["skinny"] = {"workload": sk["config"]["workload"], "value": sk["value"], "unit": sk["unit"],
+                          "ms_per_step": sk["ms_per_step"], "steps": sargs.steps, "roofline": sk["roofline"],
+                          "per_call": sk["per_call"]}
+        print("[bench] skinny record done", file=sys.stderr, flush=True)
+        line["hbm_ceiling"] = hbm_ceiling(torch, dev)
+    print(json.dumps(line), flush=True)
+
+
+def hbm_ceiling(torch, dev, nbytes=2 << 30, reps=10):
+    """Measured HBM ceilings: a streaming read (a sum over nbytes of float32) and a device copy."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        a.sum()
+        b.copy_(a)
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn, moved in (("read_GBs", lambda: a.sum(), nbytes),
+                            ("copy_GBs", lambda: b.copy_(a), 2 * nbytes)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    out["bytes"] = nbytes
+    out["kernels"] = "torch sum (read) and copy_ (read + write) over 2 GiB of float32"
+    return out
+
+
+def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
+    """Steps captured into HIP graphs and replayed (the weight-streaming workloads, whose 8-80 us kernels would
+    otherwise wait on the host, and the paged-AdamW record). Returns the JSON line (printed when emit)."""
     wl = synth.WORKLOADS[wname]
     seed_cfg = synth.WORKLOAD_SEED[wname]
     bw = bool(wl.backward)
@@ -331,7 +509,7 @@ def main():
         achieved = (fb / len(calls)) / (us_launch * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic() if args.workload == "llama7b_skinny" else None,
+                "traffic": recorded_traffic() if wname == "llama7b_skinny" else None,
                 "kernel": "k_gemv_fwd (qlora_forward, T <= 16)",
                 "bytes_per_launch": round(fb / len(calls)), "us_per_launch": round(us_launch, 3),
                 "launches": launches}
@@ -356,6 +534,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not bw:
         cpu = cpu_baseline(args, wl, seed_cfg, wbytes_step)
+    elif not args.no_cpu_baseline:
+        cpu = cpu_baseline_train(args, wl, seed_cfg, ms_step, ff + bf)
 
     line = {
         "metric": METRIC,
@@ -386,18 +566,21 @@ def main():
     if paged_info:
         line["config"]["workload"] = wl.description + ", with a paged AdamW update of every A and B"
         line["config"].update(paged_info)
-    print(json.dumps(line), flush=True)
+    if emit:
+        print(json.dumps(line), flush=True)
+    return line
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_k_gemv_fwd_llama7b_skinny.json")
+FWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_qlora_forward_65b_layer.json")
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the weight-streaming kernel from the recorded FETCH_SIZE / WRITE_SIZE runs,
-    or None when the record is missing or the kernel's sources changed since the counters were taken."""
+def recorded_traffic(record=TRAFFIC_RECORD):
+    """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counter runs (the record names the command and
+    the sources it was taken on), or None when the record is missing or those sources changed since."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(record))
         h = hashlib.sha256()
         for f in rec["sources"]:
             with open(os.path.join(ROOT, f), "rb") as fh:
@@ -445,11 +628,7 @@ def cpu_baseline(args, wl, seed_cfg, wbytes_step):
     import oracle
     from bit_quantized_finetuning_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads, blas, model = _host_info()
     # Per projection: quantized once (not timed, as on the GPU); timed: restore + forward for every T.
     prepared = []
     for pi, p in enumerate(wl.projections):
@@ -481,7 +660,89 @@ def cpu_baseline(args, wl, seed_cfg, wbytes_step):
             "cores": threads, "kind": "oracle",
             "sample": f"{done_steps} full step(s) of the same workload (restore + float64 forward of every "
                       f"projection and token count; quantization untimed), {el:.1f} s",
-            "ms_per_step": round(sec_step * 1e3, 1)}
+            "ms_per_step": round(sec_step * 1e3, 1), "cpu": model, "blas": blas}
+
+
+def _host_info():
+    """Threads the oracle's BLAS uses, the BLAS library, and the host CPU model."""
+    threads, blas = os.cpu_count(), "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info}))
+    except Exception:  # pragma: no cover
+        pass
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return threads, blas, model
+
+
+def cpu_baseline_train(args, wl, seed_cfg, ms_step_gpu, flops_step, rows=256, t_sample=128):
+    """The CPU oracle on a bounded sample of a forward + backward workload, scaled to one step.
+
+    Sample: for each distinct projection shape, a slice of `rows` output rows of its weight (same distribution),
+    quantized untimed (at model load, as on the GPU), then timed: the restore of the slice, and the float64
+    forward and backward at `t_sample` tokens. The oracle's work is linear in the rows (restore, both products)
+    and the products are linear in the tokens, so the step time is estimated as
+        sum over projections of (restore time + product time * T / t_sample) * d_out / rows
+    (the adapter terms, under 2 % of the work at these ranks, are scaled the same way)."""
+    import oracle
+    from bit_quantized_finetuning_amd import synth
+
+    (T,) = wl.tokens
+    shapes = {}
+    for pi, p in enumerate(wl.projections):
+        shapes.setdefault((p.d_out, p.d_in, p.r, p.alpha), []).append(pi)
+    prepared = []
+    for (d_out, d_in, r, alpha), pis in shapes.items():
+        pi = pis[0]
+        rr = min(rows, d_out)
+        W = synth.weight(seed_cfg, pi, rr, d_in, wl.weight_dtype)
+        codes, q2, S = oracle.quantize(W)
+        A = B = None
+        if r > 0:
+            (A, _), (B, _) = synth.adapters(seed_cfg, pi, d_out, d_in, r)
+            B = B[:rr]
+        ts = min(t_sample, T)
+        x = synth.tokens(seed_cfg, pi, ts, d_in)[0]
+        dy = synth.upstream_grad(seed_cfg, pi, ts, rr)[0]
+        prepared.append((len(pis), d_out, d_in, r, alpha, rr, ts, codes, q2, S, A, B, x, dy))
+    t_restore = [0.0] * len(prepared)
+    t_prod = [0.0] * len(prepared)
+    passes = 0
+    t_start = time.perf_counter()
+    while True:
+        for k, (units, d_out, d_in, r, alpha, rr, ts, codes, q2, S, A, B, x, dy) in enumerate(prepared):
+            t0 = time.perf_counter()
+            _, wb = oracle.dequantize(codes, q2, S, rr, d_in)
+            t1 = time.perf_counter()
+            oracle.lora_forward(wb, x, A, B, alpha, r)
+            oracle.lora_backward(wb, x, dy, A, B, alpha, r)
+            t2 = time.perf_counter()
+            t_restore[k] += t1 - t0
+            t_prod[k] += t2 - t1
+        passes += 1
+        el = time.perf_counter() - t_start
+        if el >= args.cpu_seconds:
+            break
+    sec_step = 0.0
+    for k, (units, d_out, d_in, r, alpha, rr, ts, *_rest) in enumerate(prepared):
+        sec_step += units * (t_restore[k] + t_prod[k] * T / ts) / passes * d_out / rr
+    threads, blas, model = _host_info()
+    return {"value": round(flops_step / sec_step / 1e12, 6), "unit": "TFLOP/s (same flops per step as the GPU line)",
+            "cores": threads, "kind": "oracle", "scaled": True,
+            "sample": f"{passes} pass(es) over {len(prepared)} distinct projection shapes: a {rows}-row slice of "
+                      f"each weight, restore + float64 forward and backward at {t_sample} tokens, {el:.1f} s; "
+                      f"scaled linearly to all rows, {T} tokens and every projection of the step",
+            "s_per_step": round(sec_step, 2), "gpu_speedup": round(sec_step / (ms_step_gpu * 1e-3), 1),
+            "cpu": model, "blas": blas}
 
 
 def _timed_graph(torch, dev, body, steps, chunk):
