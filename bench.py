@@ -62,7 +62,7 @@ METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD_CHOICES = ["llama7b_skinny", "65b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused",
-                    "14b_quantize",
+                    "14b_chain", "14b_quantize",
                     "merge_llama7b", "13b_paged_adamw"]
 
 
@@ -149,6 +149,8 @@ def main():
         return bench_merge(args, torch, q, synth, dev)
     if args.workload == "14b_quantize":
         return bench_quantize_stack(args, torch, q, synth, dev)
+    if args.workload == "14b_chain":
+        return bench_chain(args, torch, q, synth, dev)
     if args.workload == "13b_paged_adamw":
         return bench_graph(args, torch, q, synth, dev, "13b_4096tok", paged=True)
     if args.workload in TRAIN_WORKLOADS:
@@ -287,6 +289,71 @@ def bench_train(args, torch, q, synth, dev, wname):
         print("[bench] skinny record done", file=sys.stderr, flush=True)
         line["hbm_ceiling"] = hbm_ceiling(torch, dev)
     print(json.dumps(line), flush=True)
+
+
+def bench_chain(args, torch, q, synth, dev):
+    """All 40 layers of the 14B-style stack chained (bit_quantized_finetuning_amd.stack): one step = forward of the
+    stack under gradient checkpointing and the backward (each layer's forward again, then its backward), at 2048
+    tokens, from a bf16 input that requires grad and a seeded upstream gradient. Eager launches."""
+    from bit_quantized_finetuning_amd.stack import DecoderStack
+
+    wl = synth.WORKLOADS["14b_stack"]
+    (T,) = wl.tokens
+    layers = wl.layers
+    st = DecoderStack(layers=layers, device=dev, checkpoint=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    with torch.no_grad():  # B starts at zero; give it values so that the adapter terms are real work
+        for layer in st.layers:
+            for B in layer.qkv.B:
+                B.copy_((torch.randn(B.shape, device=dev, generator=gen) * 0.02).to(torch.bfloat16))
+    params = [p for p in st.parameters() if p.requires_grad]
+    x0 = torch.randn(T, 5120, device=dev, generator=gen).to(torch.bfloat16).requires_grad_(True)
+    dy = torch.randn(T, 5120, device=dev, generator=gen).to(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        for p in params + [x0]:
+            p.grad = None
+            if hasattr(p, "grad_fp32"):
+                p.grad_fp32 = None
+        st(x0).backward(dy)
+
+    torch.cuda.synchronize()
+    print(f"[bench] 14b_chain: {layers} layers built, {args.warmup} warm-up + {args.steps} timed steps",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ff = layers * sum(fwd_flops(p.d_out, p.d_in, p.r, T) for p in wl.projections)
+    bf = layers * sum(bwd_flops(p.d_out, p.d_in, p.r, T) for p in wl.projections)
+    tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
+    executed = (2 * ff + bf) / (ms_step * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "whole step: the projections' forward + backward flops over the step time (the recomputed "
+                      "forward and the torch glue between the calls count as time only)"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_train(args, wl, synth.WORKLOAD_SEED["14b_stack"], ms_step, ff + bf, layers=layers)
+    extra = {"data": "synthetic (seeded N(0,0.02^2) bf16 weights drawn on the device, LoRA A N(0,0.02^2), "
+                     "B N(0,0.02^2), N(0,1) input and upstream gradient)",
+             "config": {"workload": f"14B-style stack, all {layers} layers chained, hidden 5120, MLP 17408, k/v "
+                                    f"1024, LoRA r=8 alpha=16 on q/v, {T} tokens, gradient checkpointing, q/k/v "
+                                    "and gate/up as stacked calls, fwd+bwd",
+                        "layers": layers, "tokens": T, "launch": "eager"},
+             "executed_TFLOPs_incl_recompute": round(executed, 1),
+             "ms_per_layer": round(ms_step / layers, 3)}
+    _line(args, round(tflops, 1), "TFLOP/s (forward + backward of every projection of the 40 layers)", ms_step,
+          args.steps, extra["config"]["workload"], roof, cpu, extra)
 
 
 def hbm_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -684,7 +751,7 @@ def _host_info():
     return threads, blas, model
 
 
-def cpu_baseline_train(args, wl, seed_cfg, ms_step_gpu, flops_step, rows=256, t_sample=128):
+def cpu_baseline_train(args, wl, seed_cfg, ms_step_gpu, flops_step, rows=256, t_sample=128, layers=1):
     """The CPU oracle on a bounded sample of a forward + backward workload, scaled to one step.
 
     Sample: for each distinct projection shape, a slice of `rows` output rows of its weight (same distribution),
@@ -735,12 +802,14 @@ def cpu_baseline_train(args, wl, seed_cfg, ms_step_gpu, flops_step, rows=256, t_
     sec_step = 0.0
     for k, (units, d_out, d_in, r, alpha, rr, ts, *_rest) in enumerate(prepared):
         sec_step += units * (t_restore[k] + t_prod[k] * T / ts) / passes * d_out / rr
+    sec_step *= layers
     threads, blas, model = _host_info()
     return {"value": round(flops_step / sec_step / 1e12, 6), "unit": "TFLOP/s (same flops per step as the GPU line)",
             "cores": threads, "kind": "oracle", "scaled": True,
             "sample": f"{passes} pass(es) over {len(prepared)} distinct projection shapes: a {rows}-row slice of "
                       f"each weight, restore + float64 forward and backward at {t_sample} tokens, {el:.1f} s; "
-                      f"scaled linearly to all rows, {T} tokens and every projection of the step",
+                      f"scaled linearly to all rows, {T} tokens and every projection of the step"
+                      + (f" ({layers} layers)" if layers > 1 else ""),
             "s_per_step": round(sec_step, 2), "gpu_speedup": round(sec_step / (ms_step_gpu * 1e-3), 1),
             "cpu": model, "blas": blas}
 

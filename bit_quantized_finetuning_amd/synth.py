@@ -140,3 +140,32 @@ def tokens(config: int, projection: int, T: int, d_in: int, seed: int = 0):
 def upstream_grad(config: int, projection: int, T: int, d_out: int, seed: int = 0):
     """dY [T, d_out] ~ N(0, 1) in bf16: (values, bits)."""
     return to_bf16(normal(rng(config, projection, T_DY, seed), (T, d_out), 1.0))
+
+
+# The 14B-style stack as chained layers: 13.2 G weights are too many to draw on the host, so they are drawn on the
+# device with torch's seeded generator, one seed per layer (the same call on any MI355X gives the same bytes).
+STACK_SEED = 8
+STACK_SHAPES = {"q": (5120, 5120), "k": (1024, 5120), "v": (1024, 5120), "o": (5120, 5120), "gate": (17408, 5120),
+                "up": (17408, 5120), "down": (5120, 17408)}
+
+
+def stack_layer_weights(layer: int, device, shapes=None, seed: int = 0) -> dict:
+    """One layer's bf16 weights {name: [d_out, d_in]} ~ N(0, 0.02^2), drawn on `device` in the order q, k, v, o,
+    gate, up, down from torch.Generator(seed = 1_000_000 * (seed + 1) + 1000 * STACK_SEED + layer)."""
+    shapes = STACK_SHAPES if shapes is None else shapes
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1_000_000 * (seed + 1) + 1000 * STACK_SEED + layer)
+    out = {}
+    for name, (d_out, d_in) in shapes.items():
+        w = torch.empty(d_out, d_in, dtype=torch.float32, device=device)
+        w.normal_(0.0, 0.02, generator=gen)
+        out[name] = w.to(torch.bfloat16)
+        del w
+    return out
+
+
+def stack_adapter_init(layer: int, device, seed: int = 0) -> torch.Generator:
+    """The generator a stack layer draws its adapters' A from (and, for checks, B)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1_000_000 * (seed + 1) + 1000 * STACK_SEED + 500 + layer)
+    return gen
