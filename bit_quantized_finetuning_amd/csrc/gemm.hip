@@ -127,15 +127,18 @@ __device__ __forceinline__ int a_off(int lane, int s) {
 }
 
 // Restore-table build of one 64-weight block cut into 3 pieces: products of
-// the first and second half of the 16 levels, then the byte planes.
+// the first and second half of the 16 levels, then the byte planes. The scale
+// code is combined with q2o (the absmax-only marker) only after it is pinned:
+// an OR of the raw loaded byte would be pure arithmetic that the compiler may
+// hoist to the top of the step, where it would wait for the load there.
 struct TableBuild {
   float sh;
   uint32_t p[8];
-  __device__ __forceinline__ void run(int k, uint32_t q2, float S, Nf4Planes &t) {
+  __device__ __forceinline__ void run(int k, uint32_t q2, uint32_t q2o, float S, Nf4Planes &t) {
     if (k == 0) {
       pin(q2);
       pin(S);
-      sh = restore_scale(q2, S);
+      sh = restore_scale(q2 | q2o, S);
       pin(sh);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   for (int j = 0; j < 2; ++j) {
     TableBuild tb;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j] | q2o, C0.S[j], t[j]);
+    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j], q2o, C0.S[j], t[j]);
     fb[0][j] = expand8(t[j], C0.c[j][0]);
   }
 #pragma unroll
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
           if (q == 0) issue_codes(kt + 2, Ccur);
           if (q >= 1 && q <= 6) {
             const int jj = (q - 1) / 3;
-            tb.run((q - 1) % 3, Cnext.q2[jj] | q2o, Cnext.S[jj], t[jj]);
+            tb.run((q - 1) % 3, Cnext.q2[jj], q2o, Cnext.S[jj], t[jj]);
           }
           if (q == 7) wait_barrier<6>();
           if (q >= 8) {
@@ -576,7 +579,7 @@ struct DxRestore {
   u32x4 v;
   __device__ __forceinline__ void run(int k, const DxCodes &C, uint8_t *tile, uint32_t wxor, uint32_t q2o) {
     if (k < 3) {
-      tb.run(k, C.q2 | q2o, C.S, t);
+      tb.run(k, C.q2, q2o, C.S, t);
     } else if (k < 35) {
       const int m = (k - 3) >> 2, ph = (k - 3) & 3;
       const uint32_t w = m < 4 ? C.c0[m & 3] : C.c1[m & 3];

@@ -7,27 +7,43 @@
 // "메모리 회계"): the block scales are re-coded to 8 bits against their group
 // maximum so that they come back as (q2/256) * S.
 //
-// One workgroup owns one group of 256 blocks (16384 weights). Eight lanes share
-// a block: each loads 8 consecutive weights (32 contiguous bytes of float32, the
-// eight lanes together 256 contiguous bytes), the eight reduce the block absmax
-// with lane shuffles, and each lane emits its weights' codes as one packed
-// 32-bit word. All eight passes' loads are issued before any arithmetic. The
-// block scales wait in LDS for the group maximum, then one thread per block
-// writes its 8-bit scale code. The kernel streams 4 (or 2) bytes in and ~0.52
-// bytes out per weight.
+// Workgroups are persistent: each takes groups of 256 blocks (16384 weights)
+// blockIdx.x, blockIdx.x + gridDim.x, ... and builds its search table once.
+// Eight lanes share a block: each loads 8 consecutive weights (32 contiguous
+// bytes of float32, the eight lanes together 256 contiguous bytes), the eight
+// reduce the block absmax, and each lane emits its weights' codes as one packed
+// 32-bit word. All eight passes' loads of a group are issued at once; the next
+// group's loads go out as soon as the current group's weights have been coded,
+// so they fly while the group's scales are reduced and written. The block
+// scales wait in LDS for the group maximum, then one thread per block writes
+// its 8-bit scale code. The kernel streams 4 (or 2) bytes in and ~0.52 bytes
+// out per weight.
 //
 // Nearest level: the index is the number of the 15 float32 thresholds at or
-// below x = w/s (x is in [-1, 1]). Instead of 15 comparisons per weight, x's
-// float32 bits pick one of 64 buckets: sign, binade (2^-5 .. 1 in six steps,
-// everything smaller in one) and the top two significand bits. No bucket
-// holds more than one threshold, so the count is the bucket's base count
-// plus one comparison with its threshold (+inf where it has none). The
-// buckets are built per workgroup from the thresholds; checked against the
-// plain count for every float32 in [-1, 1]. For absmax-only storage (sshift 0) each block's float32
-// absmax is written as its scale instead, and there is no group step.
+// below x = fl32(w / s) (x is in [-1, 1]). The float32 bits of x pick one of
+// 2048 table entries (sign, exponent, top two significand bits): every entry
+// covers a quarter binade (all magnitudes below 2^-5 share the entries of one
+// bucket) holding at most one threshold t, and stores the count of thresholds
+// below it, t (+inf if none) and a tolerance of 16 units in the last place of
+// t. The index is then count + [x >= t].
+//
+// The quotient is not formed by the IEEE divide (about ten instructions) but
+// as xa = w * rcp(s) (v_rcp_f32, within 1 ulp), which is within 4 ulp of
+// fl32(w / s). No threshold lies within 64 ulp of a quarter-binade edge (a
+// property of the 15 thresholds, checked on the host), so xa and the exact
+// quotient fall on the same side of every threshold unless xa is within the
+// tolerance of its entry's t; such weights, and blocks whose absmax is below
+// 2^-100, are recomputed with the IEEE divide. The rule is checked against the
+// plain count on the host, with the quotient perturbed by up to 4 ulp.
+//
+// For absmax-only storage (sshift 0) each block's float32 absmax is written as
+// its scale instead, and there is no group step.
 #include "kernels.h"
 
 namespace qlora {
+
+constexpr int kQTable = 2048;
+constexpr int64_t kQuantizeGrid = 1024;
 
 template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, int64_t nblocks,
@@ -38,22 +54,28 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   constexpr int kPasses = kGroup / 32;
   __shared__ float s_blk[kGroup];
   __shared__ float s_red[4];
-  __shared__ float2 bucket[64];  // {threshold inside the bucket or +inf, count of thresholds below it}
+  __shared__ float2 bucket[64];       // {threshold inside the bucket or +inf, count of thresholds below it}
+  __shared__ u32x4 qtab[kQTable];     // {bits of t, bits of the tolerance, count, 0} per (sign, exponent, m2)
   const int tid = threadIdx.x;
-  const int64_t b0 = (int64_t)blockIdx.x * kGroup;
-  const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
   const int l8 = tid & 7;
   const int slot = tid >> 3;  // 32 blocks per pass
-  const rsrc_t wr = make_rsrc(static_cast<const uint8_t *>(W) + b0 * kBlock * esz, (int64_t)nb * kBlock * esz);
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
 
   u32x4 raw[kPasses][kBf16In ? 1 : 2];
+  auto load_group = [&](int64_t g) {
+    const int64_t b0 = g * kGroup;
+    const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
+    const rsrc_t wr = make_rsrc(static_cast<const uint8_t *>(W) + b0 * kBlock * esz, (int64_t)nb * kBlock * esz);
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int b = p * 32 + slot;
-    const uint32_t off = b < nb ? (uint32_t)((b * kBlock + l8 * 8) * esz) : kOOB;
-    raw[p][0] = bld16(wr, off);
-    if (!kBf16In) raw[p][kBf16In ? 0 : 1] = bld16(wr, off + 16);
-  }
+    for (int p = 0; p < kPasses; ++p) {
+      const int b = p * 32 + slot;
+      const uint32_t off = b < nb ? (uint32_t)((b * kBlock + l8 * 8) * esz) : kOOB;
+      raw[p][0] = bld16(wr, off);
+      if (!kBf16In) raw[p][kBf16In ? 0 : 1] = bld16(wr, off + 16);
+    }
+  };
+  int64_t g = blockIdx.x;
+  if (g < ngroups) load_group(g);
 
   // Bucket b = sign * 32 + e * 4 + m covers magnitudes [lo, hi): e = 0 is
   // [0, 2^-5); e = 1 .. 6 the binade [2^(e-6), 2^(e-5)) cut into quarters by m.
@@ -84,73 +106,103 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
     bucket[tid] = make_float2(cand, (float)below);
   }
   __syncthreads();
+  // Entry i = (sign, exponent, m2) from bits 31, 30..23, 22..21 of x: its bucket,
+  // with exponents below 122 in bucket e = 0 and above 127 (never reached) in e = 6.
+  for (int i = tid; i < kQTable; i += 256) {
+    const int sg = i >> 10, ex = (i >> 2) & 0xff, m2 = i & 3;
+    const int e = min(max(ex - 121, 0), 6);
+    const float2 bk = bucket[(sg << 5) | (e << 2) | (e == 0 ? 0 : m2)];
+    const uint32_t tb = __float_as_uint(bk.x);
+    const uint32_t texp = (tb >> 23) & 0xffu;
+    // 16 ulp of t = 2^(texp - 127 - 23 + 4); none (0) where t is +inf
+    const uint32_t tol = bk.x < __builtin_inff() ? (texp - 19u) << 23 : 0u;
+    qtab[i] = u32x4{tb, tol, (uint32_t)bk.y, 0u};
+  }
+  __syncthreads();
 
-  uint32_t bad = 0;
+  for (; g < ngroups; g += gridDim.x) {
+    const int64_t b0 = g * kGroup;
+    const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
+    uint32_t bad = 0;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int b = p * 32 + slot;
-    float w[8];
-    if (kBf16In) {
+    for (int p = 0; p < kPasses; ++p) {
+      const int b = p * 32 + slot;
+      float w[8];
+      if (kBf16In) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[2 * e] = bf16_lo_to_f32(raw[p][0][e]);
-        w[2 * e + 1] = bf16_hi_to_f32(raw[p][0][e]);
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = bf16_lo_to_f32(raw[p][0][e]);
+          w[2 * e + 1] = bf16_hi_to_f32(raw[p][0][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = __uint_as_float(raw[p][0][e]);
+          w[4 + e] = __uint_as_float(raw[p][kBf16In ? 0 : 1][e]);
+        }
       }
+      // Block absmax as the largest magnitude bit pattern: for finite values the
+      // order of |w|'s bits is the order of |w|; a NaN or inf makes it >= 0x7f800000.
+      uint32_t mb = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mb = max(mb, __float_as_uint(w[e]) & 0x7fffffffu);
+      mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false));   // lanes ^ 1
+      mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, false));   // lanes ^ 2
+      mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x141, 0xF, 0xF, false));  // other quad of 8
+      bad |= mb >= 0x7f800000u;
+      const float m = __uint_as_float(mb);
+      const float rm = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+      bool near = m > 0.f && m < 0x1p-100f;
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xa = w[e] * rm;
+        const u32x4 ent = qtab[__float_as_uint(xa) >> 21];
+        const float d = xa - __uint_as_float(ent[0]);
+        near |= fabsf(d) <= __uint_as_float(ent[1]);
+        word |= (ent[2] + (d >= 0.f ? 1u : 0u)) << nibble_shift(e);
+      }
+      if (near) {  // rare: the exact quotient decides
+        word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = m > 0.f ? w[e] / m : 0.f;  // IEEE float32 divide
+          const u32x4 ent = qtab[__float_as_uint(x) >> 21];
+          word |= (ent[2] + (x >= __uint_as_float(ent[0]) ? 1u : 0u)) << nibble_shift(e);
+        }
+      }
+      if (b < nb) {
+        if (l8 == 0) s_blk[b] = m;
+        *reinterpret_cast<uint32_t *>(codes + (b0 + b) * (kBlock / 2) + l8 * 4) = word;
+      }
+    }
+    if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
+    __syncthreads();
+
+    const float s = tid < nb ? s_blk[tid] : 0.f;
+    if (sshift == 0) {  // absmax-only storage: the block scales as they are
+      if (tid < nb) smax[b0 + tid] = s;
     } else {
+      float S = s;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[e] = __uint_as_float(raw[p][0][e]);
-        w[4 + e] = __uint_as_float(raw[p][kBf16In ? 0 : 1][e]);
+      for (int off = 32; off > 0; off >>= 1) S = fmaxf(S, __shfl_xor(S, off));
+      if ((tid & 63) == 0) s_red[tid >> 6] = S;
+      __syncthreads();
+      S = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      if (tid < nb) {
+        uint32_t q2 = 0;
+        if (S > 0.f) {
+          const float ratio = s / S;             // fl32(s / S)
+          const float v = rintf(ratio * 256.f);  // exact scale, ties to even
+          q2 = (uint32_t)fminf(v, 255.f);
+        }
+        qscale[b0 + tid] = (uint8_t)q2;
       }
+      if (tid == 0) smax[g] = S;
     }
-    float m = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bad |= !__builtin_isfinite(w[e]);
-      m = fmaxf(m, fabsf(w[e]));
-    }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = m > 0.f ? w[e] / m : 0.f;  // IEEE float32 divide
-      const uint32_t xb = __float_as_uint(x);
-      const int be = min(max((int)((xb >> 23) & 0xffu) - 121, 0), 6);
-      const float2 bk = bucket[((xb >> 31) << 5) | ((uint32_t)be << 2) | ((xb >> 21) & 3u)];
-      const uint32_t q = (uint32_t)bk.y + (x >= bk.x ? 1u : 0u);
-      word |= q << nibble_shift(e);
-    }
-    if (b < nb) {
-      if (l8 == 0) s_blk[b] = m;
-      *reinterpret_cast<uint32_t *>(codes + (b0 + b) * (kBlock / 2) + l8 * 4) = word;
-    }
-  }
-  __syncthreads();
-
-  const float s = tid < nb ? s_blk[tid] : 0.f;
-  if (sshift == 0) {  // absmax-only storage: the block scales as they are
-    if (tid < nb) smax[b0 + tid] = s;
     if (bad && flags) atomicOr(flags, 1u);
-    return;
+    __syncthreads();  // s_blk and s_red are reused by the next group
   }
-  float S = s;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) S = fmaxf(S, __shfl_xor(S, off));
-  if ((tid & 63) == 0) s_red[tid >> 6] = S;
-  __syncthreads();
-  S = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  if (tid < nb) {
-    uint32_t q2 = 0;
-    if (S > 0.f) {
-      const float ratio = s / S;             // fl32(s / S)
-      const float v = rintf(ratio * 256.f);  // exact scale, ties to even
-      q2 = (uint32_t)fminf(v, 255.f);
-    }
-    qscale[b0 + tid] = (uint8_t)q2;
-  }
-  if (tid == 0) smax[blockIdx.x] = S;
-  if (bad && flags) atomicOr(flags, 1u);
 }
 
 // Restore: one thread per 8 weights (one packed word). float32 output is the
@@ -196,12 +248,13 @@ hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d
   const int64_t nblocks = d_out * d_in / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   const int sshift = qscale ? kDqShift : 0;
+  // persistent workgroups: four per compute unit of a 256-CU part (their LDS
+  // allows four), or one per group when there are fewer groups
+  const unsigned grid = (unsigned)(ngroups < kQuantizeGrid ? ngroups : kQuantizeGrid);
   if (bf16_in)
-    k_quantize<true><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift,
-                                                                    c);
+    k_quantize<true><<<dim3(grid), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift, c);
   else
-    k_quantize<false><<<dim3((unsigned)ngroups), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift,
-                                                                     c);
+    k_quantize<false><<<dim3(grid), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift, c);
   return hipGetLastError();
 }
 
