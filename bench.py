@@ -272,6 +272,8 @@ def bench_train(args, torch, q, synth, dev, wname):
         "cpu_baseline": None,
     }
     print(f"[bench] {wname}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_train(args, wl, cfg, ms_step, ff + bf)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
@@ -354,6 +356,17 @@ def bench_chain(args, torch, q, synth, dev):
              "ms_per_layer": round(ms_step / layers, 3)}
     _line(args, round(tflops, 1), "TFLOP/s (forward + backward of every projection of the 40 layers)", ms_step,
           args.steps, extra["config"]["workload"], roof, cpu, extra)
+
+
+def copy_calibration(torch, dev):
+    """A plain device copy of known size (256 MiB read + 256 MiB written per launch, three launches): the
+    reference that scales the HBM byte counters of a profiled run."""
+    a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def hbm_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -589,14 +602,7 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
     per_call = per_call_times(torch, dev, calls, run_call, chunk) if not (args.no_graph or args.no_per_call) else []
 
     if args.copy_calibration:
-        # a plain device copy of known size (256 MiB read + 256 MiB written per launch), the reference that
-        # scales the HBM byte counters
-        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        copy_calibration(torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline and not bw:

@@ -277,17 +277,37 @@ __device__ __forceinline__ void plain_tile(f32x16 (&acc)[8][2], const uint8_t *a
 constexpr int kTileFloats = kBM * kBN;  // one float32 partial tile
 constexpr int kMaxSplit = 8;
 
-// Workgroup b runs tile b whole if b < full; otherwise part (b - full) % split
-// of tail tile full + (b - full) / split, over K steps [k0, k1).
+// Workgroup b < full runs one whole tile; otherwise part (b - full) % split of
+// tail tile full + (b - full) / split, over K steps [k0, k1).
+//
+// Whole tiles are handed out XCD-aware. Consecutive workgroups go to the eight
+// XCDs in turn (b % 8), and the workgroups of one XCD run at about the same
+// time, each streaming its activation row tile and its weight column tile
+// through that XCD's L2. XCD x therefore takes the x-th contiguous share of
+// the tiles in an order that walks down kXcdRows row tiles before moving to
+// the next column: the 32 tiles it holds at once span 2 row tiles x 16 column
+// tiles instead of all 8 row tiles x 4 columns, which cuts what its L2 pulls
+// in per step (one activation row tile is four times the bytes of one weight
+// column tile). Tiles of an incomplete last row keep the linear order.
+constexpr int kXcdRows = 2;
 struct WorkItem {
   int tile, part, parts, k0, k1;
   int64_t m0, n0;
 };
+__device__ __forceinline__ int xcd_tile(int b, int gn, int full) {
+  const int x = b & 7, i = b >> 3, q = full >> 3, rem8 = full & 7;
+  const int L = x * q + (x < rem8 ? x : rem8) + i;  // a bijection of [0, full)
+  const int rows = full / gn;                        // complete rows among the whole tiles
+  if (L >= rows * gn) return L;
+  const int g = L / (kXcdRows * gn), ha = rows - g * kXcdRows < kXcdRows ? rows - g * kXcdRows : kXcdRows;
+  const int idx = L - g * kXcdRows * gn;
+  return (g * kXcdRows + idx % ha) * gn + idx / ha;
+}
 __device__ __forceinline__ WorkItem work_item(int gn, int nk, int full, int split) {
   WorkItem w;
   const int b = blockIdx.x;
   if (b < full) {
-    w.tile = b;
+    w.tile = xcd_tile(b, gn, full);
     w.part = 0;
     w.parts = 1;
     w.k0 = 0;
