@@ -411,13 +411,37 @@ __device__ __forceinline__ void split_combine(const f32x16 (&acc)[8][2], float *
 // Forward
 // ---------------------------------------------------------------------------
 // Codes of one K step held by one lane: for each of its two output rows
-// (column tiles j = 0, 1) the four code words of its K half, the block's scale
-// code and its group maximum.
+// (column tiles j = 0, 1) the four code words of its K half; and the scale
+// code and group maximum of the block of row j = l / 32 only. Lanes l and
+// l + 32 hold the same two rows, so each builds one of the two restore tables
+// and v_permlane32_swap gives both lanes both (see share_tables).
 struct FwdCodes {
   u32x4 c[2];
-  uint32_t q2[2];
-  float S[2];
+  uint32_t q2;
+  float S;
 };
+
+// Table words of row j = l / 32 in every lane -> t[0] (row j = 0) and t[1]
+// (row j = 1) in every lane: the swap hands lanes 0..31 the words of lanes
+// 32..63 in its second result and lanes 32..63 those of lanes 0..31 in its
+// first. Words k0 .. k0 + 3 of the eight (lo[0..3], hi[0..3]).
+__device__ __forceinline__ void share_tables(const Nf4Planes &own, Nf4Planes (&t)[2], int k0) {
+#pragma unroll
+  for (int k = k0; k < k0 + 4; ++k) {
+    const uint32_t w = k < 4 ? own.lo[k] : own.hi[k - 4];
+    const auto sw = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    uint32_t a = sw[0], b = sw[1];
+    pin(a);
+    pin(b);
+    if (k < 4) {
+      t[0].lo[k] = a;
+      t[1].lo[k] = b;
+    } else {
+      t[0].hi[k - 4] = a;
+      t[1].hi[k - 4] = b;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ qscale,
@@ -454,23 +478,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   const DmaOffs xo = dma_offsets((int)d_in, wave, lane);
 
   // This lane's output rows (column tiles j = 0, 1) within the tile: byte
-  // offsets of their code rows and scale-code rows, and their first block index.
-  uint32_t coff[2], qoff[2], blk0[2];
+  // offsets of their code rows; the scale-code row and first block index of
+  // row j = l / 32.
+  uint32_t coff[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = kWN * wave + 32 * j + ml;
-    coff[j] = (uint32_t)(row * (d_in / 2)) + 16u * half;
-    qoff[j] = (uint32_t)(row * KB);
-    blk0[j] = (uint32_t)((n0 + row) * KB);
-  }
+  for (int j = 0; j < 2; ++j) coff[j] = (uint32_t)((kWN * wave + 32 * j + ml) * (d_in / 2)) + 16u * half;
+  const int trow = kWN * wave + 32 * half + ml;
+  const uint32_t qoff = (uint32_t)(trow * KB), blk0 = (uint32_t)((n0 + trow) * KB);
   auto issue_codes = [&](int kt, FwdCodes &C) {
     const int kc = kt < nk ? kt : nk - 1;  // steps past the end reload the last one (never used)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      C.c[j] = bld16s(cr, coff[j], kc * (kBlock / 2));
-      C.q2[j] = bld8s(qr, qoff[j], kc);
-      C.S[j] = __uint_as_float(bld32(sr, ((blk0[j] + (uint32_t)kc) >> sshift) * 4u));
-    }
+    for (int j = 0; j < 2; ++j) C.c[j] = bld16s(cr, coff[j], kc * (kBlock / 2));
+    C.q2 = bld8s(qr, qoff, kc);
+    C.S = __uint_as_float(bld32(sr, ((blk0 + (uint32_t)kc) >> sshift) * 4u));
   };
 
   f32x16 acc[8][2];
@@ -484,14 +504,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   dma_tile(xr, xo, k0 * kBK, smem, wave);
   issue_codes(k0, C0);
   issue_codes(k0 + 1, C1);
-  wait_barrier<6>();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  wait_barrier<4>();
+  {
     TableBuild tb;
+    Nf4Planes own;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2[j], q2o, C0.S[j], t[j]);
-    fb[0][j] = expand8(t[j], C0.c[j][0]);
+    for (int k = 0; k < 3; ++k) tb.run(k, C0.q2, q2o, C0.S, own);
+    share_tables(own, t, 0);
+    share_tables(own, t, 4);
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[0][j] = expand8(t[j], C0.c[j][0]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) fa[0][i] = *reinterpret_cast<const u32x4 *>(smem + aoff[0] + 4096 * i);
 
@@ -499,15 +522,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   // holds the codes of step kt+1. Side work after MFMA q of slice s:
   //   s < 3 : A fragments of slice s+1 (q < 8); B fragments of slice s+1
   //           (expand pieces at odd q: column tile 0 at q = 1..7, 1 at 9..15);
-  //   s = 3 : codes of step kt+2 into Ccur (q = 0); tables of step kt+1
-  //           (q = 1..6); wait for tile kt+1 and barrier (q = 7); then the
-  //           A and B fragments of step kt+1, slice 0 (q = 8..15).
+  //   s = 3 : codes of step kt+2 into Ccur (q = 0); this lane's table of
+  //           step kt+1 (q = 1..3) and the swap that shares it (q = 4, 5);
+  //           wait for tile kt+1 and barrier (q = 7); then the A and B
+  //           fragments of step kt+1, slice 0 (q = 8..15).
   auto step = [&](int kt, const int P, FwdCodes &Ccur, FwdCodes &Cnext) {
     // (the last step copies its own tile again into the idle slot: no branch)
     dma_tile(xr, xo, (kt + 1 < k1 ? kt + 1 : kt) * kBK, smem + (P ^ 1) * kTile, wave);
     const uint8_t *cur = smem + P * kTile, *nxt = smem + (P ^ 1) * kTile;
     Expand ex;
     TableBuild tb;
+    Nf4Planes own;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -523,11 +548,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
           }
         } else {
           if (q == 0) issue_codes(kt + 2, Ccur);
-          if (q >= 1 && q <= 6) {
-            const int jj = (q - 1) / 3;
-            tb.run((q - 1) % 3, Cnext.q2[jj], q2o, Cnext.S[jj], t[jj]);
-          }
-          if (q == 7) wait_barrier<6>();
+          if (q >= 1 && q <= 3) tb.run(q - 1, Cnext.q2, q2o, Cnext.S, own);
+          if (q == 4 || q == 5) share_tables(own, t, 4 * (q - 4));
+          if (q == 7) wait_barrier<4>();
           if (q >= 8) {
             fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
             const int jj = (q - 8) >> 2, ph = (q - 8) & 3;
