@@ -167,6 +167,25 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP
 
 namespace qlora {
 
+int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
+int device_cu_count(int dev) {
+  static DeviceOnce once;
+  static int cus[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  (void)once.run(dev, [&] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+    return hipSuccess;
+  });
+  return cus[dev];
+}
+
 // Argument checks of a forward call that do not involve the workspace.
 int validate_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const uint16_t *A, const uint16_t *B,
                      int32_t r, uint16_t *h, float *u_out) {
@@ -258,6 +277,13 @@ int qlora_workspace_fallbacks(const void *ws, uint32_t *count, hipStream_t strea
   if (!ws || !count) return QLORA_ERR_NULL;
   const void *word = static_cast<const uint8_t *>(ws) + (kMaxCounters - 1) * sizeof(uint32_t);
   if (hipMemcpyAsync(count, word, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) return QLORA_ERR_HIP;
+  return hip_status(hipStreamSynchronize(stream));
+}
+
+int qlora_workspace_set_wait_limit(void *ws, uint32_t ticks, hipStream_t stream) {
+  if (!ws) return QLORA_ERR_NULL;
+  void *word = static_cast<uint8_t *>(ws) + (kMaxCounters - 2) * sizeof(uint32_t);
+  if (hipMemsetD32Async(word, (int)ticks, 1, stream) != hipSuccess) return QLORA_ERR_HIP;
   return hip_status(hipStreamSynchronize(stream));
 }
 

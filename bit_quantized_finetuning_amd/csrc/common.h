@@ -40,8 +40,8 @@ __host__ __device__ inline int64_t scale_words(int64_t nblocks, int sshift) {
 // gradient kernel's time). A kernel whose tile count exceeds kMaxTileCounters
 // runs without a split. The last kSyncWords words of the region are reserved:
 // the last of them counts the waits that ran out of time and took their
-// fallback (the result is the same either way; see split_claim and the skinny
-// forward's exchange).
+// fallback (the result is the same either way; see split_arrive and the skinny
+// forward's exchange), the one before it overrides the wait limit (wait_limit).
 constexpr int64_t kMaxCounters = 16384;
 constexpr int64_t kSyncWords = 4;
 constexpr int64_t kCounterStride = 32;  // 32-bit words per tile counter
@@ -241,6 +241,15 @@ __device__ __forceinline__ uint32_t xchg_dev_u32(uint32_t *p, uint32_t v) {
 // wait ends in a few microseconds; the limit matters only when launches on
 // other streams hold the compute units that the awaited workgroups need.
 constexpr long long kWaitTicks = 20000;
+// The limit in force for the launches on a workspace: the counter-region word
+// just before the fallback count (`fallbacks - 1`) replaces kWaitTicks when it
+// is nonzero. A testing aid: a limit of 1 tick sends every wait that does not
+// succeed at once down its fallback path, whose results must equal the others.
+__device__ __forceinline__ long long wait_limit(const uint32_t *fallbacks) {
+  const uint32_t v = __hip_atomic_load(const_cast<uint32_t *>(fallbacks - 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return v ? (long long)v : kWaitTicks;
+}
 
 // ---------------------------------------------------------------------------
 // Combine of a tile whose reduction range is split over `parts` workgroups,
@@ -251,7 +260,7 @@ constexpr long long kWaitTicks = 20000;
 //   word 0        arrivals (low 16 bits) and departures (high 16 bits)
 //   word 1 + s    claim of share s (0 free, 1 taken)
 // A part that arrives last knows every partial is stored; an earlier part
-// polls for the last arrival until kWaitTicks pass. Whoever has seen all
+// polls for the last arrival until the wait limit passes. Whoever has seen all
 // arrivals claims its own share (one atomic exchange) and sums it if the claim
 // wins; the last arriver afterwards claims every share still free and sums
 // those too. So every share is summed exactly once, by its own part when all
@@ -270,13 +279,13 @@ __device__ __forceinline__ uint32_t split_arrive(uint32_t *line, int part, int p
   last = (prev & 0xffffu) == (uint32_t)(parts - 1);
   bool ready = last;
   if (!last) {
-    const long long t0 = wall_clock64();
+    const long long t0 = wall_clock64(), limit = wait_limit(fallbacks);
     for (;;) {
       if ((ld_dev_u32(line) & 0xffffu) >= (uint32_t)parts) {
         ready = true;
         break;
       }
-      if (wall_clock64() - t0 > kWaitTicks) {
+      if (wall_clock64() - t0 > limit) {
         add_dev_u32(fallbacks, 1u);
         break;
       }

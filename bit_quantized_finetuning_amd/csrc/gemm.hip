@@ -809,33 +809,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   }
 }
 
-static bool g_attr_set[64];
-
 static hipError_t set_lds_attrs() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (g_attr_set[dev]) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_fwd),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFwdLds);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_dx), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)kDxLds);
-  if (e != hipSuccess) return e;
-  g_attr_set[dev] = true;
-  return hipSuccess;
-}
-
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
+  static DeviceOnce once;
+  return once.run(current_device(), [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_fwd),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFwdLds);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(k_gemm_dx),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDxLds);
+  });
 }
 
 // Choose the K split of the tail tiles by a step count: whole tiles take nk
@@ -848,7 +830,7 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t nk) {
   p.gm = (int)((M + kBM - 1) / kBM);
   p.gn = (int)((N + kBN - 1) / kBN);
   p.nk = (int)nk;
-  const int64_t tiles = (int64_t)p.gm * p.gn, cus = device_cus();
+  const int64_t tiles = (int64_t)p.gm * p.gn, cus = device_cu_count(current_device());
   const int64_t rounds = tiles / cus, rem = tiles % cus;
   int best = 1;
   int64_t best_cost = rounds * nk + (rem > 0 ? nk : 0);

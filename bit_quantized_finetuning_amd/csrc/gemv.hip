@@ -42,7 +42,7 @@
 //     re-read until their tags match), the four partials summed in slice order
 //     and bf16(s*u) put in LDS; wave 0 then adds s*u B^T as r_pad more K
 //     columns. The workgroup of row tile 0 writes float32 u for the backward.
-//   * a reader that has waited kWaitTicks for a partial forms it itself with
+//   * a reader that has waited the wait limit (kWaitTicks) for a partial forms it itself with
 //     the producer's own code (same operands, same order of operations, so the
 //     same bits) and publishes it as the producer would. The grid never
 //     exceeds one residency and producers never wait, so on its own a launch
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   __shared__ uint32_t miss[2];  // jobs with a partial not yet seen (bit j kKsp + ks)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int li = lane & 15, g = lane >> 4;
+  if (tid == 0) miss[0] = miss[1] = 0u;  // read only after later barriers (the fallback of the exchange)
   const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
   const int KB = d_in / kBlock;
   const int cid = blockIdx.x, G = gridDim.x;
@@ -244,17 +245,9 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
   // one 64-bit store. Nothing waits for those stores: a reader accepts an
   // entry once its tag matches. (Run by every wave of the workgroup.)
   const uint32_t tag = launch_tag();
-  auto a_run = [&](int job) {
+  // The waves' partials of a job: reduce through LDS in wave order and publish with the tag.
+  auto a_publish = [&](int job, const f32x4 &pacc) {
     const int pj = job / kKsp, pks = job % kKsp;
-    const int k32b = nk32 * pks / kKsp, k32e = nk32 * (pks + 1) / kKsp;
-    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-    for (int b = 0;; ++b) {
-#pragma unroll
-      for (int s = 0; s < kABatch; ++s)
-        if (k32b + wave + kW * (kABatch * b + s) < k32e) pacc = mfma16(xp[s], ap[s], pacc);  // wave-uniform
-      if (k32b + kABatch * kW * (b + 1) >= k32e) break;
-      a_issue(job, b + 1);
-    }
     // lane (li, g) holds u[4g + i][16j + li]
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + li] = pacc[i];
@@ -267,6 +260,36 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       if (t < T) st_dev_u64(uex + (pks * 16 + t) * r_pad + col, (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32));
     }
     lds_barrier();
+  };
+  auto a_run = [&](int job) {
+    const int pks = job % kKsp;
+    const int k32b = nk32 * pks / kKsp, k32e = nk32 * (pks + 1) / kKsp;
+    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0;; ++b) {
+#pragma unroll
+      for (int s = 0; s < kABatch; ++s)
+        if (k32b + wave + kW * (kABatch * b + s) < k32e) pacc = mfma16(xp[s], ap[s], pacc);  // wave-uniform
+      if (k32b + kABatch * kW * (b + 1) >= k32e) break;
+      a_issue(job, b + 1);
+    }
+    a_publish(job, pacc);
+  };
+  // The same job one K step at a time, for the rare reader that forms a missing
+  // partial itself: the same MFMA operands in the same order as a_run, so the
+  // same bits, in a fraction of a_run's code (it sits in the epilogue, which the
+  // item loop holds twice, and its size alone slowed every launch by 7 %).
+  auto a_run_cold = [&](int job) {
+    const int pj = job / kKsp, pks = job % kKsp;
+    const int k32b = nk32 * pks / kKsp, k32e = nk32 * (pks + 1) / kKsp;
+    const int arows = r - 16 * pj < 16 ? r - 16 * pj : 16;
+    const rsrc_t ar = make_rsrc(A + (int64_t)16 * pj * d_in, (int64_t)arows * d_in * 2);
+    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int k32 = k32b + wave; k32 < k32e; k32 += kW) {
+      const uint32_t off = (uint32_t)((li * d_in + k32 * 32 + 8 * g) * 2);
+      pacc = mfma16(bld16(xr, off), bld16(ar, off), pacc);
+    }
+    a_publish(job, pacc);
   };
   // x comes straight from global memory (rows >= T read zeros), so the job
   // waits for nothing but its own loads, issued first.
@@ -333,15 +356,16 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
       // workgroup of row tile 0 also writes float32 u. Rows t >= T of su_l
       // only feed accumulator rows that are never stored.
       // One round: write every entry whose partials all carry this launch's
-      // tag, note the jobs of those that do not, and (thread 0) whether the
-      // wait has run out of time; returns whether any entry of the workgroup
-      // was not ready (two flag rows in turn: a row is rewritten only two
-      // barriers after it was last read).
-      const long long t0 = wall_clock64();
-      if (tid == 0) miss[0] = miss[1] = 0u;
-      lds_barrier();
+      // tag, note in a register the jobs of those that do not, and (thread 0)
+      // whether the wait has run out of time; returns whether any entry of the
+      // workgroup was not ready (two flag rows in turn: a row is rewritten only
+      // two barriers after it was last read). The job masks meet in LDS only
+      // when the wait has run out.
+      const long long t0 = wall_clock64(), limit = wait_limit(&sync[3]);
+      uint64_t mymiss = 0;
       auto check = [&](const uint64_t (&pv)[kPairsAhead][kKsp], int it) {
         int bad = 0;
+        mymiss = 0;
         for (int i = 0; i * kThreads < npair; ++i) {
           uint64_t e[kKsp];
           if (i < kPairsAhead) {
@@ -357,10 +381,8 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
           for (int ks = 0; ks < kKsp; ++ks) {
             const bool oks = (uint32_t)(e[ks] >> 32) == tag;
             ok = ok && oks;
-            if (!oks) {
-              const int job = ((p - (p / r_pad) * r_pad) >> 4) * kKsp + ks;
-              atomicOr(&miss[job >> 5], 1u << (job & 31));
-            }
+            const int job = ((p - (p / r_pad) * r_pad) >> 4) * kKsp + ks;
+            mymiss |= oks ? 0ull : 1ull << job;
             u += __uint_as_float((uint32_t)e[ks]);
           }
           if (!ok) {
@@ -373,7 +395,7 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
         }
         const int wbad = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0ull ? 1 : 0);
         if (lane == 0) poll_bad[it & 1][wave] = wbad;
-        if (tid == 0) poll_late[it & 1] = wall_clock64() - t0 > kWaitTicks ? 1 : 0;
+        if (tid == 0) poll_late[it & 1] = wall_clock64() - t0 > limit ? 1 : 0;
         lds_barrier();
         int any = 0;
 #pragma unroll
@@ -386,11 +408,15 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
         if (poll_late[it & 1]) {
           // form the missing partials here, exactly as their producers would,
           // and publish them; the next round then finds every entry
+          if (mymiss) {
+            atomicOr(&miss[0], (uint32_t)mymiss);
+            atomicOr(&miss[1], (uint32_t)(mymiss >> 32));
+          }
+          lds_barrier();
           const uint32_t m0 = miss[0], m1 = miss[1];
           for (int job = 0; job < P; ++job) {
             if (!(((job < 32 ? m0 : m1) >> (job & 31)) & 1u)) continue;
-            a_issue(job, 0);
-            a_run(job);
+            a_run_cold(job);
           }
           if (tid == 0) {
             miss[0] = miss[1] = 0u;

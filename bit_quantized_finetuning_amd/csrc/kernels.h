@@ -5,10 +5,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "qlora.h"
 
 namespace qlora {
+
+// Per-device one-time set-up of a launcher (function attributes): the first
+// call on a device runs `fn` under a once flag, every call returns its status.
+// Safe to use from any number of host threads.
+constexpr int kMaxDevices = 64;
+struct DeviceOnce {
+  std::once_flag flag[kMaxDevices];
+  hipError_t status[kMaxDevices] = {};
+  template <class F>
+  hipError_t run(int dev, F &&fn) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(flag[dev], [&] { status[dev] = fn(); });
+    return status[dev];
+  }
+};
+// api.cpp: the current device (-1 if it cannot be read) and its compute-unit
+// count (read once per device; 256 if the query fails).
+int current_device();
+int device_cu_count(int dev);
 
 // api.cpp: the forward's argument checks, the workspace bytes one forward call
 // touches, and its kernels on a checked workspace (used by the entry points of

@@ -195,12 +195,7 @@ __global__ __launch_bounds__(256) void k_lora_tall(const uint16_t *__restrict__ 
 }
 
 int lora_tall_ksplit(int64_t T, int64_t K) {
-  int cus = 256;
-  int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
-  }
+  const int cus = device_cu_count(current_device());
   const int64_t tiles = (T + kTallT - 1) / kTallT, nk = (K + 63) / 64;
   int64_t ks = cus / tiles;
   if (ks > nk / 4) ks = nk / 4;
@@ -220,15 +215,12 @@ static hipError_t launch_tall(const uint16_t *P, const uint16_t *Q, int64_t T, i
                               float scale, float *out_f32, uint16_t *out_bf16, float *partial, uint32_t *counters,
                               hipStream_t st) {
   constexpr int kLds = RS * (8192 + 4096 * NCQ);
-  static bool attr[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_tall<NCQ, RS>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr[dev] = true;
-  }
+  static DeviceOnce once;
+  const hipError_t e = once.run(current_device(), [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_tall<NCQ, RS>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  });
+  if (e != hipSuccess) return e;
   const int ks = lora_tall_ksplit(T, K);
   const int64_t tiles = (T + kTallT - 1) / kTallT;
   k_lora_tall<NCQ, RS><<<dim3((unsigned)tiles, (unsigned)ks), dim3(256), kLds, st>>>(
@@ -504,12 +496,7 @@ __global__ __launch_bounds__(256) void k_lora_wgrad(const uint16_t *__restrict__
 // once (then the ranges of a tile share the combine), at least two 64-token
 // steps each.
 int lora_wgrad_ksplit(int64_t D, int64_t R, int64_t T) {
-  int cus = 256;
-  int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
-  }
+  const int cus = device_cu_count(current_device());
   const int64_t tiles = ((D + kWgD - 1) / kWgD) * ((R + kWgR - 1) / kWgR);
   const int64_t nkt = (T + kWgTok - 1) / kWgTok;
   int64_t ks = cus / (tiles > 0 ? tiles : 1);
@@ -526,22 +513,18 @@ size_t lora_wgrad_partial_floats(int64_t D, int64_t R, int64_t T) {
   return ks > 1 ? (size_t)tiles * ks * kWgTileFloats : 0;
 }
 
-static bool g_wg_attr[64];
-
 hipError_t launch_lora_wgrad(const uint16_t *X, const float *Y, int64_t T, int64_t D, int64_t R, bool y_is_rows,
                              float scale, float *C, float *partial, uint32_t *counters, uint32_t *fallbacks,
                              hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!g_wg_attr[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_wgrad<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLds);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_wgrad<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLds);
-    if (e != hipSuccess) return e;
-    g_wg_attr[dev] = true;
-  }
+  static DeviceOnce once;
+  const hipError_t e = once.run(current_device(), [] {
+    const hipError_t s = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_wgrad<true>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLds);
+    if (s != hipSuccess) return s;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(k_lora_wgrad<false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLds);
+  });
+  if (e != hipSuccess) return e;
   const int ks = lora_wgrad_ksplit(D, R, T);
   const int64_t tiles = ((D + kWgD - 1) / kWgD) * ((R + kWgR - 1) / kWgR);
   const dim3 grid((unsigned)tiles, (unsigned)ks);

@@ -32,8 +32,6 @@
 //     out with eight consecutive lanes on each 128-byte row, so every store
 //     instruction writes whole lines (16-byte pieces of 64 different lines ran
 //     at four fifths of the rate).
-#include <mutex>
-
 #include "kernels.h"
 #include "tiles.h"
 
@@ -199,11 +197,6 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
   }
 }
 
-namespace {
-std::once_flag g_merge_once[64];
-hipError_t g_merge_attr[64];
-}  // namespace
-
 template <int RS>
 static hipError_t set_merge_attr() {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(k_merge<RS>), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -212,20 +205,17 @@ static hipError_t set_merge_attr() {
 
 hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float *smax, int64_t d_out, int64_t d_in,
                         const uint16_t *A, const uint16_t *B, int r, float scale, uint16_t *out, hipStream_t st) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::call_once(g_merge_once[dev], [&] {
+  static DeviceOnce once;
+  const hipError_t e = once.run(current_device(), [] {
     hipError_t s = set_merge_attr<0>();
     if (s == hipSuccess) s = set_merge_attr<1>();
     if (s == hipSuccess) s = set_merge_attr<2>();
     if (s == hipSuccess) s = set_merge_attr<4>();
     if (s == hipSuccess) s = set_merge_attr<8>();
     if (s == hipSuccess) s = set_merge_attr<kMgMaxSteps>();
-    g_merge_attr[dev] = s;
+    return s;
   });
-  if (g_merge_attr[dev] != hipSuccess) return g_merge_attr[dev];
+  if (e != hipSuccess) return e;
   const int strips = (int)(d_in / kMgCols);
   const int64_t rows_per_wg = (int64_t)kMgRows * kMgWaves * kMgRT;
   const int64_t groups = (d_out + rows_per_wg - 1) / rows_per_wg;

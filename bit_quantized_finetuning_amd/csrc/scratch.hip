@@ -18,7 +18,6 @@ namespace {
 
 static __device__ __align__(256) uint8_t scratch[QLORA_STATIC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 
 struct DeviceScratch {
   std::once_flag once;

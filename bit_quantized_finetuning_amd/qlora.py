@@ -7,7 +7,8 @@ there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
     qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_forward_noalloc, qlora_backward,
-    qlora_adamw_step, qlora_workspace_fallbacks, qlora_storage_bytes, qlora_storage_bytes_absmax,
+    qlora_adamw_step, qlora_workspace_fallbacks, qlora_workspace_set_wait_limit, qlora_storage_bytes,
+    qlora_storage_bytes_absmax,
     qlora_workspace_bytes, qlora_nf4_codebook, qlora_nf4_thresholds, qlora_status_string
 
 The C ABI sees only pointers, so every tensor argument is checked here before the call: its shape against the
@@ -65,6 +66,8 @@ _lib.qlora_forward_noalloc.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp,
 _lib.qlora_forward_noalloc.restype = ctypes.c_int
 _lib.qlora_workspace_fallbacks.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
 _lib.qlora_workspace_fallbacks.restype = ctypes.c_int
+_lib.qlora_workspace_set_wait_limit.argtypes = [_vp, ctypes.c_uint32, _vp]
+_lib.qlora_workspace_set_wait_limit.restype = ctypes.c_int
 _lib.qlora_backward.argtypes = [_W, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_backward.restype = ctypes.c_int
 _lib.qlora_storage_bytes.argtypes = [_i64, _i64]
@@ -404,6 +407,18 @@ def qlora_workspace_fallbacks(ws: torch.Tensor) -> int:
     n = ctypes.c_uint32(0)
     _check(_lib.qlora_workspace_fallbacks(_ptr(ws), ctypes.byref(n), _stream(ws.device)), "qlora_workspace_fallbacks")
     return int(n.value)
+
+
+def qlora_workspace_set_wait_limit(ws: torch.Tensor, ticks: int) -> None:
+    """A testing aid: later calls on this workspace give up a wait after `ticks` ticks of the 100 MHz clock and
+    take the fallback path (1 sends every wait that does not succeed at once there); 0 restores the built-in
+    limit. Synchronizes the current stream."""
+    _own_workspace(ws, COUNTER_BYTES)
+    _check_devices(ws.device)
+    if not 0 <= int(ticks) < 1 << 32:
+        raise ValueError("ticks must fit in 32 bits")
+    _check(_lib.qlora_workspace_set_wait_limit(_ptr(ws), int(ticks), _stream(ws.device)),
+           "qlora_workspace_set_wait_limit")
 
 
 def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: torch.Tensor | None,

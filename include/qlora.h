@@ -241,6 +241,17 @@ int qlora_forward_noalloc(const qlora_nf4_weight *W, const uint16_t *x, int64_t 
  */
 int qlora_workspace_fallbacks(const void *ws, uint32_t *count, hipStream_t stream);
 
+/*
+ * Host, a testing aid: the bounded waits of later calls on this workspace give
+ * up after `ticks` ticks of the 100 MHz constant clock instead of the built-in
+ * 20000 (about 200 us); 0 restores the built-in limit. The limit is the u32
+ * just before the fallback count. With ticks = 1 every wait that does not
+ * succeed at once takes its fallback path (see qlora_workspace_fallbacks),
+ * so a test can check that those paths give the same bits. Sets one word on
+ * `stream` and synchronizes it. Errors: NULL, HIP.
+ */
+int qlora_workspace_set_wait_limit(void *ws, uint32_t ticks, hipStream_t stream);
+
 /* Bytes of the quantized weight: n/2 + n/64 + 4*ceil(n/16384). */
 size_t qlora_storage_bytes(int64_t d_out, int64_t d_in);
 

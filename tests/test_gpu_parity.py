@@ -409,3 +409,51 @@ def test_concurrent_full_size_calls_from_two_threads():
     for ws in wss:
         assert int(ws[:q.COUNTER_BYTES - 4].view(torch.int32).abs().sum().item()) == 0
         say(f"    fallbacks: {q.qlora_workspace_fallbacks(ws)}")
+
+
+def test_fallback_paths_give_the_same_bits():
+    """With the workspace's wait limit at one tick, every wait that does not succeed at once takes its fallback
+    path: a skinny forward's reader forms missing adapter partials itself (4096 x 4096, T = 1 and 16, r = 64), a
+    split GEMM part (1024 x 4096 at T = 512: fewer tiles than compute units, every tile split over K) and a
+    token-split adapter-gradient part leave their shares to the last arriver. Three repetitions give bit for bit
+    the outputs of the same calls under the built-in limit, and the fallback count shows that the paths ran."""
+    say("fallback paths")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(23)
+    w1 = q.qlora_quantize(torch.randn(4096, 4096, device="cuda", generator=gen) * 0.02)
+    x1 = _rand_bf16(gen, 16, 4096)
+    A1, B1 = _rand_bf16(gen, 64, 4096, std=0.02), _rand_bf16(gen, 4096, 64, std=0.02)
+    w2 = q.qlora_quantize(torch.randn(1024, 4096, device="cuda", generator=gen) * 0.02)
+    x2, dy2 = _rand_bf16(gen, 512, 4096), _rand_bf16(gen, 512, 1024)
+    A2, B2 = _rand_bf16(gen, 64, 4096, std=0.02), _rand_bf16(gen, 1024, 64, std=0.02)
+    ws = torch.zeros(max(q.qlora_workspace_bytes(4096, 4096, 16, 64), q.qlora_workspace_bytes(1024, 4096, 512, 64)),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def run():
+        out = []
+        for T in (1, 16):
+            out += list(q.qlora_forward(w1, x1[:T].contiguous(), A1, B1, 16.0, save_u=True, ws=ws))
+        h, u = q.qlora_forward(w2, x2, A2, B2, 16.0, save_u=True, ws=ws)
+        out += [h, u] + list(q.qlora_backward(w2, x2, dy2, A2, B2, 16.0, u_saved=u, ws=ws))
+        return out
+
+    ref = run()
+    torch.cuda.synchronize()
+    assert q.qlora_workspace_fallbacks(ws) == 0
+    q.qlora_workspace_set_wait_limit(ws, 1)
+    try:
+        got = [run() for _ in range(3)]
+        torch.cuda.synchronize()
+        n = q.qlora_workspace_fallbacks(ws)
+    finally:
+        q.qlora_workspace_set_wait_limit(ws, 0)
+    say(f"    fallbacks with a one-tick limit: {n}")
+    for rep, out in enumerate(got):
+        for i, (a, b) in enumerate(zip(out, ref)):
+            same = torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+            assert same, f"repetition {rep}, output {i} differs from the run under the built-in limit"
+    assert n > 0, "no wait took its fallback path"
+    # every counter is left zero (the last word counts the fallbacks, the one before it is the limit, now 0)
+    assert int(ws[:q.COUNTER_BYTES - 4].view(torch.int32).abs().sum().item()) == 0
