@@ -81,11 +81,14 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--storage", default="dq", choices=["dq", "absmax"],
                    help="weight storage: NF4 with double-quantized scales (4.13 bits) or float32 block absmax (4.5)")
-    p.add_argument("--paging", default="zerocopy", choices=["zerocopy", "dma"],
-                   help="13b_paged_adamw: update m, v in host memory in place, or copy each page to the device and back")
+    p.add_argument("--paging", default="zerocopy", choices=["zerocopy", "dma", "host"],
+                   help="13b_paged_adamw: update m, v in host memory in place (GPU kernel), copy each page to the "
+                        "device and back, or run the update on the host CPU (the page's placement; eager only)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     a = p.parse_args()
+    if a.paging == "host":
+        a.no_graph = True  # host work between the copies cannot be captured
     skinny = a.workload in ("llama7b_skinny", "65b_skinny", "merge_llama7b")
     if a.steps is None:
         a.steps = 200 if skinny else 20
@@ -394,6 +397,19 @@ def hbm_ceiling(torch, dev, nbytes=2 << 30, reps=10):
     return out
 
 
+class HostJobs:
+    """The host-update jobs of one projection's adapters: wait() makes the current stream wait for all of them."""
+
+    def __init__(self, worker):
+        self.worker, self.jobs = worker, []
+
+    def add(self, job):
+        self.jobs.append(job)
+
+    def wait(self):
+        self.worker.wait_jobs(self.jobs)
+
+
 def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
     """Steps captured into HIP graphs and replayed (the weight-streaming workloads, whose 8-80 us kernels would
     otherwise wait on the host, and the paged-AdamW record). Returns the JSON line (printed when emit)."""
@@ -443,6 +459,12 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
     # float32 master copy on the device
     opt_state = {}
     opt_stream = torch.cuda.Stream(dev) if paged else None  # default priority
+    host_update = paged and args.paging == "host"
+    worker = None
+    if host_update:
+        from bit_quantized_finetuning_amd.optim import HostAdamWWorker
+        worker = HostAdamWWorker(dev, opt_stream)
+    staging = {}
     if paged:
         for pi, (p, copies, *_rest) in enumerate(projs):
             for ci, (wc, A, B) in enumerate(copies):
@@ -450,9 +472,13 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
                     continue
                 st = []
                 for t in (A, B):
-                    master = t.float()
+                    # the host update keeps the master copy with m and v in pinned host memory
+                    master = t.float().cpu().pin_memory() if host_update else t.float()
                     st.append((t, master, torch.zeros(t.numel(), dtype=torch.float32).pin_memory(),
                                torch.zeros(t.numel(), dtype=torch.float32).pin_memory()))
+                    if host_update:
+                        staging[(pi, ci, len(st) - 1)] = (torch.empty(t.numel(), dtype=torch.float32).pin_memory(),
+                                                          torch.empty(t.numel(), dtype=torch.bfloat16).pin_memory())
                 opt_state[(pi, ci)] = st
     # DMA paging: one device page (m, v) sized for the largest parameter, reused in turn on the update stream
     # (its copies and kernels run in order there)
@@ -479,12 +505,26 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
         pi = next(i for i, pr in enumerate(projs) if pr[0] is p)
         if opt_on[0] and (pi, ci) in opt_pending:
             # the previous update of these parameters must land before the forward reads them
-            torch.cuda.current_stream(dev).wait_event(opt_pending.pop((pi, ci)))
+            pend = opt_pending.pop((pi, ci))
+            if host_update:
+                pend.wait()
+            else:
+                torch.cuda.current_stream(dev).wait_event(pend)
         dX, dA, dB, u = g
         ur = u if p.r > 0 else None
         q.qlora_forward(wc, x, A, B, p.alpha, h=h, u=ur)
         q.qlora_backward(wc, x, dy, A, B, p.alpha, u_saved=ur, dX=dX, dA=dA if p.r > 0 else None,
                          dB=dB if p.r > 0 else None)
+        if opt_on[0] and (pi, ci) in opt_state and host_update:
+            ready = torch.cuda.Event()
+            ready.record(torch.cuda.current_stream(dev))
+            jobs = HostJobs(worker)
+            for k, ((t, master, m, v), grad) in enumerate(zip(opt_state[(pi, ci)], (dA, dB))):
+                g_host, p_host = staging[(pi, ci, k)]
+                jobs.add(worker.submit_job(1, grad.view(-1), g_host, master, m, v, t.view(-1), p_host, ready,
+                                           lr=1e-4, weight_decay=0.01))
+            opt_pending[(pi, ci)] = jobs
+            return
         if opt_on[0] and (pi, ci) in opt_state:
             ready = torch.cuda.Event()
             ready.record(torch.cuda.current_stream(dev))
@@ -513,6 +553,9 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
             for c in calls:
                 run_call(*c, s * nT + c[-1])
         if opt_on[0]:
+            if host_update:
+                for pend in opt_pending.values():
+                    pend.wait()
             # join the update stream (also closes a graph capture's fork)
             torch.cuda.current_stream(dev).wait_stream(opt_stream)
             opt_pending.clear()
@@ -561,13 +604,17 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
         n_opt = sum(st[0].numel() for sts in opt_state.values() for st in sts) // max(len(projs[0][1]), 1)
         paged_info = {"ms_per_step_without_optimizer": round(ms_off / args.steps, 5),
                       "optimizer_throughput_loss_pct": round(100.0 * (1.0 - ms_off / ms_total), 2),
-                      "optimizer": "AdamW (lr 1e-4, wd 0.01): m and v of every A and B in pinned host memory, float32 "
-                                   "master on the device, updated by qlora_adamw_step on a side stream beside the next "
-                                   "projection; "
-                                   + ("each state page copied to the device and back by DMA around the update"
-                                      if args.paging == "dma" else "the kernel reads and writes host memory in place"),
+                      "optimizer": ("AdamW (lr 1e-4, wd 0.01) on the host CPU (qlora_adamw_step_host, the page's "
+                                    "placement): float32 dA, dB copied to pinned host memory, master, m and v of every A "
+                                    "and B in pinned host memory, the bf16 parameters copied back; a worker thread runs "
+                                    "the host steps beside the next projection's kernels" if args.paging == "host" else
+                                    "AdamW (lr 1e-4, wd 0.01): m and v of every A and B in pinned host memory, float32 "
+                                    "master on the device, updated by qlora_adamw_step on a side stream beside the next "
+                                    "projection; "
+                                    + ("each state page copied to the device and back by DMA around the update"
+                                       if args.paging == "dma" else "the kernel reads and writes host memory in place")),
                       "adapter_params_per_step": n_opt,
-                      "host_link_bytes_per_step": 16 * n_opt}
+                      "host_link_bytes_per_step": (6 * n_opt if args.paging == "host" else 16 * n_opt)}
     else:
         ms_total, have_graphs = measure()
     ms_step = ms_total / args.steps

@@ -7,7 +7,7 @@ there is no fallback path.
 
 Function names follow the C ABI in include/qlora.h:
     qlora_quantize, qlora_dequantize, qlora_merge, qlora_forward, qlora_forward_noalloc, qlora_backward,
-    qlora_adamw_step, qlora_workspace_fallbacks, qlora_workspace_set_wait_limit, qlora_storage_bytes,
+    qlora_adamw_step, qlora_adamw_step_host, qlora_workspace_fallbacks, qlora_workspace_set_wait_limit, qlora_storage_bytes,
     qlora_storage_bytes_absmax,
     qlora_workspace_bytes, qlora_nf4_codebook, qlora_nf4_thresholds, qlora_status_string
 
@@ -60,6 +60,8 @@ _lib.qlora_merge.argtypes = [_W, _vp, _vp, _i32, _f32, _vp, _vp]
 _lib.qlora_merge.restype = ctypes.c_int
 _lib.qlora_adamw_step.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.qlora_adamw_step.restype = ctypes.c_int
+_lib.qlora_adamw_step_host.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32]
+_lib.qlora_adamw_step_host.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
 _lib.qlora_forward_noalloc.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp]
@@ -345,6 +347,27 @@ def qlora_adamw_step(step: int, grad: torch.Tensor, master: torch.Tensor, m: tor
     st = ctypes.c_void_p((stream or torch.cuda.current_stream(grad.device)).cuda_stream)
     _check(_lib.qlora_adamw_step(ctypes.byref(hp), step, n, _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
                                  _ptr(param), st), "qlora_adamw_step")
+
+
+def qlora_adamw_step_host(step: int, grad: torch.Tensor, master: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                          param: torch.Tensor | None = None, lr: float = 1e-4, beta1: float = 0.9,
+                          beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0, threads: int = 0):
+    """The same AdamW step run by the host CPU: every tensor in host memory (pinned, so that the caller's copies
+    to and from the device are DMA copies); param (bf16, optional) receives bf16(master). Blocks until done."""
+    for t in (grad, master, m, v):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("grad, master, m and v must be contiguous float32 tensors")
+    n = grad.numel()
+    if any(t.numel() != n for t in (master, m, v)) or (param is not None and param.numel() != n):
+        raise ValueError("all tensors must have the same number of elements")
+    if param is not None:
+        _bits(param)
+    for name, t in (("grad", grad), ("master", master), ("m", m), ("v", v), ("param", param)):
+        if t is not None and t.device.type != "cpu":
+            raise ValueError(f"{name} must be in host memory, got {t.device}")
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(_lib.qlora_adamw_step_host(ctypes.byref(hp), step, n, _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
+                                      _ptr(param), int(threads)), "qlora_adamw_step_host")
 
 
 def _forward_args(w, x, A, B, h, u, save_u, ws=None):

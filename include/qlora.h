@@ -213,6 +213,22 @@ int qlora_adamw_step(const qlora_adamw_hparams *hp, int64_t step, int64_t n, con
                      float *m, float *v, uint16_t *param, hipStream_t stream);
 
 /*
+ * The same AdamW step run by the host CPU, the page's own placement of the
+ * paged optimizer's update ("메모리 회계": the CPU runs the optimizer step on
+ * the state in pinned CPU memory while the GPU goes on with the backward). The
+ * caller copies grad to host memory first and param back to the device after:
+ * plain DMA copies, so the GPU's compute units never run the update.
+ *   grad    host f32 [n];  master, m, v  host f32 [n], updated in place
+ *   param   host bf16 [n], nullable: receives bf16(master) (round to nearest even)
+ *   threads worker threads to use (<= 0: all of the pool, at most 16)
+ * The per-element arithmetic is qlora_adamw_step's, in float32 (results agree
+ * to rounding). Blocks until done; calls from several host threads take turns.
+ * Errors: NULL, VALUE (hyperparameters, step < 1), SHAPE (n < 0).
+ */
+int qlora_adamw_step_host(const qlora_adamw_hparams *hp, int64_t step, int64_t n, const float *grad, float *master,
+                          float *m, float *v, uint16_t *param, int32_t threads);
+
+/*
  * For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): qlora_forward without a
  * workspace argument, for the weight-streaming regime of T <= 16 tokens (the

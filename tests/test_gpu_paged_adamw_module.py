@@ -17,16 +17,18 @@ optim = product("optim")
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
 
-@pytest.mark.parametrize("paged", [True, False])
-def test_paged_adamw_trains_a_layer_like_the_oracle(paged):
-    say(f"PagedAdamW paged={paged}")
+@pytest.mark.parametrize("paged,update", [(True, "device"), (False, "device"), (True, "host")])
+def test_paged_adamw_trains_a_layer_like_the_oracle(paged, update):
+    """update="host" runs the page's own placement: gradients copied to pinned host memory, the library's host
+    AdamW, the bf16 parameters copied back."""
+    say(f"PagedAdamW paged={paged} update={update}")
     torch.manual_seed(3)
     W = (torch.randn(272, 320) * 0.02).cuda()
     m = layer.QLoRALinear(W, r=16, alpha=32.0)
     with torch.no_grad():
         m.B.copy_((torch.randn(272, 16) * 0.02).to(torch.bfloat16))
     opt = optim.PagedAdamW(m.parameters(), lr=HP["lr"], betas=(HP["beta1"], HP["beta2"]), eps=HP["eps"],
-                           weight_decay=HP["weight_decay"], paged=paged)
+                           weight_decay=HP["weight_decay"], paged=paged, update=update)
     assert all(st[1].is_pinned() == paged for st in opt.state)
     ref = [[p.detach().double().cpu().numpy().reshape(-1), np.zeros(p.numel()), np.zeros(p.numel())]
            for p in opt.params]
