@@ -36,7 +36,8 @@ Other workloads (--workload) are records, not the headline line:
   14b_stack_fused  the same layer with q/k/v and gate/up each stacked into one call that reads its input once
       (q and v adapters as one block-diagonal rank-16 pair);
   14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack (13.2 G parameters, generated
-      on the device from a seeded generator);
+      on the device from a seeded generator) with qlora_quantize_many (32 weights per launch), and beside it the
+      same pass as one qlora_quantize call per weight;
   merge_llama7b  merge for export, bf16(W_hat + (alpha/r) B A), of the two LLaMA-7B projections with r = 64;
   13b_paged_adamw  the 13b_4096tok step, timed without and with an AdamW update of every A and B whose moments
       m, v sit in pinned host memory (float32 master on the device); the update of a projection runs on a side
@@ -978,7 +979,8 @@ def bench_merge(args, torch, q, synth, dev):
 
 def bench_quantize_stack(args, torch, q, synth, dev):
     """One pass quantizing all 280 bf16 weights of the 14B-style stack (40 layers x q, k, v, o, gate, up, down):
-    one step = the whole pass, 280 launches of k_quantize. Weights come from a seeded device generator
+    one step = the whole pass, one qlora_quantize_many call (9 launches of k_quantize, 32 weights each); the
+    same pass with one qlora_quantize call per weight is timed beside it. Weights come from a seeded device generator
     (N(0, 0.02^2) rounded to bf16); 13.2 G weights are too many to draw on the host."""
     wl = synth.WORKLOADS["14b_stack"]
     gen = torch.Generator(device=dev)
@@ -993,17 +995,23 @@ def bench_quantize_stack(args, torch, q, synth, dev):
     torch.cuda.synchronize()
 
     def body(k):
+        q.qlora_quantize_many(Ws, outs)
+
+    def body_single(k):
         for W, o in zip(Ws, outs):
             q.qlora_quantize(W, out=o)
 
     ms_step, steps = _timed_graph(torch, dev, body, args.steps, 1)
+    ms_single, _ = _timed_graph(torch, dev, body_single, args.steps, 1)
+    launches = -(-len(Ws) // 32)  # 32 weights per launch
     n = sum(W.numel() for W in Ws)
     nbytes = sum(2 * W.numel() + q.qlora_storage_bytes(W.shape[0], W.shape[1]) for W in Ws)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_quantize<bf16> (qlora_quantize)",
-            "bytes_per_launch": round(nbytes / len(Ws)), "us_per_launch": round(ms_step * 1e3 / len(Ws), 3),
-            "launches": steps * len(Ws)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_quantize<bf16> (qlora_quantize_many: 32 weights per launch)",
+            "bytes_per_launch": round(nbytes / launches), "us_per_launch": round(ms_step * 1e3 / launches, 3),
+            "launches": steps * launches}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -1026,7 +1034,9 @@ def bench_quantize_stack(args, torch, q, synth, dev):
                "sample": f"{done} quantization(s) of a 256x5120 bf16 slice, {el:.1f} s"}
     _line(args, round(gbs, 1), "GB/s (quantize algorithmic bytes per second: bf16 in, NF4 + double quant out)",
           ms_step, steps, f"one-pass quantize of the 14B-style stack: {len(Ws)} bf16 weights, {n / 1e9:.2f} G "
-          "parameters", roof, cpu, {"weights": len(Ws), "params": n, "ms_per_pass": round(ms_step, 3)})
+          "parameters", roof, cpu, {"weights": len(Ws), "params": n, "ms_per_pass": round(ms_step, 3),
+                                    "ms_per_pass_one_call_per_weight": round(ms_single, 3),
+                                    "GBs_one_call_per_weight": round(nbytes / (ms_single * 1e-3) / 1e9, 1)})
 
 
 if __name__ == "__main__":

@@ -304,14 +304,45 @@ size_t qlora_workspace_bytes(int64_t d_out, int64_t d_in, int64_t T, int32_t r) 
   return layout(d_out, d_in, T, r).total;
 }
 
+int qlora_quantize_many(const void *const *W, int w_dtype, const qlora_nf4_weight *out, int32_t count,
+                        uint32_t *flags, hipStream_t stream) {
+  if (count < 0) return QLORA_ERR_SHAPE;
+  if (count > 0 && (!W || !out)) return QLORA_ERR_NULL;
+  // every job is checked before anything is launched
+  for (int32_t i = 0; i < count; ++i) {
+    if (!W[i]) return QLORA_ERR_NULL;
+    const int s = validate_weight(&out[i]);
+    if (s) return s;
+    if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+    if (!aligned16(W[i]) || (flags && (reinterpret_cast<uintptr_t>(flags) & 3u))) return QLORA_ERR_ALIGN;
+  }
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  for (int32_t i0 = 0; i0 < count; i0 += kQuantizeJobs) {
+    QuantizeJobs jobs{};
+    jobs.n = (int)std::min<int32_t>(kQuantizeJobs, count - i0);
+    int64_t g = 0;
+    for (int k = 0; k < jobs.n; ++k) {
+      const qlora_nf4_weight &o = out[i0 + k];
+      jobs.W[k] = W[i0 + k];
+      jobs.codes[k] = o.codes;
+      jobs.qscale[k] = o.qscale;
+      jobs.smax[k] = o.smax;
+      jobs.nblocks[k] = o.d_out * o.d_in / QLORA_BLOCK;
+      jobs.gstart[k] = g;
+      g += ceil_div(jobs.nblocks[k], kGroup);
+    }
+    jobs.gstart[jobs.n] = g;
+    const int s = hip_status(launch_quantize(jobs, w_dtype == QLORA_BF16, flags, consts(), stream));
+    if (s) return s;
+  }
+  return QLORA_OK;
+}
+
 int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint32_t *flags, hipStream_t stream) {
   if (!W) return QLORA_ERR_NULL;
-  int s = validate_weight(out);
+  const int s = validate_weight(out);  // (out may be NULL)
   if (s) return s;
-  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
-  if (!aligned16(W) || (flags && (reinterpret_cast<uintptr_t>(flags) & 3u))) return QLORA_ERR_ALIGN;
-  return hip_status(launch_quantize(W, w_dtype == QLORA_BF16, out->d_out, out->d_in, out->codes, out->qscale,
-                                    out->smax, flags, consts(), stream));
+  return qlora_quantize_many(&W, w_dtype, out, 1, flags, stream);
 }
 
 int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStream_t stream) {

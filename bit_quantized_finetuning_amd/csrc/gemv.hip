@@ -492,22 +492,16 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_fwd(
 
 constexpr int kGvW = 8;  // waves per workgroup
 
-static int g_gemv_cus[64];
-static bool g_gemv_attr[64];
-
-static int device_index() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  return dev;
-}
-
-static int device_cus(int dev) {
-  if (dev < 0) return 256;
-  if (g_gemv_cus[dev] > 0) return g_gemv_cus[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
-  g_gemv_cus[dev] = cus;
-  return cus;
+static hipError_t set_gemv_attrs() {
+  static DeviceOnce once;
+  return once.run(current_device(), [] {
+    for (const void *f : {reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, true>),
+                          reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, false>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsBytes);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
 }
 
 bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T) {
@@ -520,13 +514,13 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
                            int r_pad, float scale, uint16_t *h, float *u_out, uint64_t *uex, uint32_t *sync,
                            hipStream_t st) {
   if (r_pad > kMaxRpad || !gemv_supported(d_out, d_in, T)) return hipErrorInvalidValue;
-  const int dev = device_index();
   const int P = r > 0 ? (r_pad / 16) * kKsp : 0;
   const int64_t RT = (d_out + 15) / 16;
   // One workgroup per CU; the first P of them also produce x A^T. The grid never
   // exceeds one residency, so on an otherwise idle chip every workgroup runs
   // concurrently (the kernel does not depend on it: see the file comment).
-  int64_t G = RT < device_cus(dev) ? RT : device_cus(dev);
+  const int64_t cus = device_cu_count(current_device());
+  int64_t G = RT < cus ? RT : cus;
   if (G < P) G = P;
   const size_t xbytes = (size_t)T * (d_in + kXPad) * 2;
   const int di = (int)d_in, dn = (int)d_out, Tt = (int)T;
@@ -535,14 +529,8 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
   const int sshift = qscale ? kDqShift : 0;
   const uint8_t *qs = qscale ? qscale : codes;
   if (xbytes <= (size_t)kXLdsBytes) {
-    if (dev >= 0 && !g_gemv_attr[dev]) {
-      for (const void *f : {reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, true>),
-                            reinterpret_cast<const void *>(k_gemv_fwd<kGvW, true, false>)}) {
-        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsBytes);
-        if (e != hipSuccess) return e;
-      }
-      g_gemv_attr[dev] = true;
-    }
+    const hipError_t e = set_gemv_attrs();
+    if (e != hipSuccess) return e;
     if (q4)
       k_gemv_fwd<kGvW, true, true><<<dim3((unsigned)G), dim3(64 * kGvW), xbytes, st>>>(
           codes, qs, smax, dn, di, x, Tt, A, B, r, r_pad, scale, h, u_out, uex, sync, sshift);

@@ -41,8 +41,20 @@ int enqueue_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, con
                     int32_t r, float alpha, uint16_t *h, float *u_out, void *ws, hipStream_t stream);
 
 // quantize.hip
-hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d_in, uint8_t *codes,
-                           uint8_t *qscale, float *smax, uint32_t *flags, const Nf4Consts &c,
+// Up to kQuantizeJobs weights per launch, passed by value as a kernel
+// argument (no device buffer): job i covers global groups
+// [gstart[i], gstart[i+1]); qscale[i] == NULL selects absmax-only storage.
+constexpr int kQuantizeJobs = 32;
+struct QuantizeJobs {
+  const void *W[kQuantizeJobs];
+  uint8_t *codes[kQuantizeJobs];
+  uint8_t *qscale[kQuantizeJobs];
+  float *smax[kQuantizeJobs];
+  int64_t nblocks[kQuantizeJobs];
+  int64_t gstart[kQuantizeJobs + 1];
+  int n;
+};
+hipError_t launch_quantize(const QuantizeJobs &jobs, bool bf16_in, uint32_t *flags, const Nf4Consts &c,
                            hipStream_t st);
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *qscale, const float *smax,
                              int64_t d_out, int64_t d_in, bool bf16_out, void *out, const Nf4Consts &c,

@@ -28,6 +28,8 @@
 // its share of rows over all ranges in range order once all have arrived; a
 // range that stops waiting leaves its share to the last one to arrive
 // (split_arrive in common.h), so no range depends on another being dispatched.
+#include <type_traits>
+
 #include "kernels.h"
 #include "tiles.h"
 
@@ -165,31 +167,52 @@ __global__ __launch_bounds__(256) void k_lora_tall(const uint16_t *__restrict__ 
   if (tid == 0) is_last = add_dev_u32(tile_counter(counters, tile), 1u) == (uint32_t)ksplit - 1u;
   __syncthreads();
   if (!is_last) return;
-  // Sum the parts: each thread takes 4-float chunks; all parts' loads of a
-  // chunk go out before the first one is used.
+  // Sum the parts in part order. ksplit is a power of two; each thread takes
+  // 16 / ksplit 4-float chunks at a time and issues every part's load of all
+  // of them before the first is used (loads past the chunks read zeros), so
+  // the sum costs one round trip per batch, not one per load.
   const rsrc_t prs = make_rsrc(partial + (int64_t)tile * ksplit * kTallT * r_pad,
                                (int64_t)ksplit * kTallT * r_pad * 4);
-  for (int c = tid; c < kTallT * r_pad / 4; c += 256) {
-    u32x4 w[kTallMaxSplit];
+  auto combine = [&](auto ks_c) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_c)::value;
+    constexpr int CPB = kTallMaxSplit / KS;
+    const int nch = kTallT * r_pad / 4;
+    for (int c0 = tid; c0 < nch; c0 += 256 * CPB) {
+      u32x4 w[CPB][KS];
 #pragma unroll
-    for (int p = 0; p < kTallMaxSplit; ++p)
-      if (p < ksplit) w[p] = bld16_dev(prs, (uint32_t)((p * kTallT * r_pad + 4 * c) * 4));
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < CPB; ++j)
 #pragma unroll
-    for (int p = 0; p < kTallMaxSplit; ++p)
-      if (p < ksplit)
-        v += f32x4{__uint_as_float(w[p][0]), __uint_as_float(w[p][1]), __uint_as_float(w[p][2]),
-                   __uint_as_float(w[p][3])};
-    const int row = (4 * c) / r_pad, col0 = (4 * c) % r_pad;
-    const int64_t tt = t0 + row;
-    if (tt < T) {
+        for (int p = 0; p < KS; ++p) {
+          const int c = c0 + 256 * j;
+          w[j][p] = bld16_dev(prs, c < nch ? (uint32_t)((p * kTallT * r_pad + 4 * c) * 4) : kOOB);
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int col = col0 + u;
-        if (out_f32 && col < r) out_f32[tt * r + col] = v[u];
-        if (out_bf16) out_bf16[tt * r_pad + col] = (uint16_t)(pack_bf16x2(col < r ? scale * v[u] : 0.f, 0.f) & 0xffffu);
+      for (int j = 0; j < CPB; ++j) {
+        const int c = c0 + 256 * j;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KS; ++p)
+          v += f32x4{__uint_as_float(w[j][p][0]), __uint_as_float(w[j][p][1]), __uint_as_float(w[j][p][2]),
+                     __uint_as_float(w[j][p][3])};
+        const int row = (4 * c) / r_pad, col0 = (4 * c) % r_pad;
+        const int64_t tt = t0 + row;
+        if (c < nch && tt < T) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int col = col0 + u;
+            if (out_f32 && col < r) out_f32[tt * r + col] = v[u];
+            if (out_bf16)
+              out_bf16[tt * r_pad + col] = (uint16_t)(pack_bf16x2(col < r ? scale * v[u] : 0.f, 0.f) & 0xffffu);
+          }
+        }
       }
     }
+  };
+  switch (ksplit) {
+    case 2: combine(std::integral_constant<int, 2>{}); break;
+    case 4: combine(std::integral_constant<int, 4>{}); break;
+    case 8: combine(std::integral_constant<int, 8>{}); break;
+    default: combine(std::integral_constant<int, 16>{}); break;
   }
   if (tid == 0) st_dev_u32(tile_counter(counters, tile), 0u);
 }
@@ -202,6 +225,7 @@ int lora_tall_ksplit(int64_t T, int64_t K) {
   if (ks > kTallMaxSplit) ks = kTallMaxSplit;
   if (ks < 1) ks = 1;
   if (tiles > kMaxTileCounters) ks = 1;
+  while (ks & (ks - 1)) ks &= ks - 1;  // a power of two (the combine batches loads by it)
   return (int)ks;
 }
 
@@ -451,30 +475,49 @@ __global__ __launch_bounds__(256) void k_lora_wgrad(const uint16_t *__restrict__
     claim_lds[1] = last ? 1u : 0u;
   }
   wait_barrier<0>();
-  auto sum_shares = [&](uint32_t mask) {
-    for (int sh = 0; sh < ksplit; ++sh) {
+  // ksplit is a power of two, so a share is 16 / ksplit chunks per thread:
+  // every part's load of all of them goes out before the first is used.
+  auto sum_shares_ks = [&](uint32_t mask, auto ks_c) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_c)::value;
+    constexpr int CPB = kWgMaxSplit / KS;
+    for (int sh = 0; sh < KS; ++sh) {
       if (!((mask >> sh) & 1u)) continue;
-      const int glo = sh * (kWgTileFloats / 4) / ksplit, ghi = (sh + 1) * (kWgTileFloats / 4) / ksplit;
-      for (int g = glo + tid; g < ghi; g += 256) {
-        u32x4 w[kWgMaxSplit];
+      const int glo = sh * (kWgTileFloats / 4) / KS, ghi = (sh + 1) * (kWgTileFloats / 4) / KS;
+      for (int g0 = glo + tid; g0 < ghi; g0 += 256 * CPB) {
+        u32x4 w[CPB][KS];
 #pragma unroll
-        for (int p = 0; p < kWgMaxSplit; ++p)
-          if (p < ksplit) w[p] = bld16_dev(prs, (uint32_t)((p * kWgTileFloats + 4 * g) * 4));
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CPB; ++j)
 #pragma unroll
-        for (int p = 0; p < kWgMaxSplit; ++p)
-          if (p < ksplit)
-            v += f32x4{__uint_as_float(w[p][0]), __uint_as_float(w[p][1]), __uint_as_float(w[p][2]),
-                       __uint_as_float(w[p][3])};
-        const int gl = g & 63, e4 = (g >> 6) & 3, b = (g >> 8) & 1, a = (g >> 9) & 1, gw = g >> 10;
-        const int row = 32 * a + 8 * e4 + 4 * (gl >> 5) + (kYisA ? 0 : 64 * gw);
-        const int col = 32 * b + (gl & 31) + (kYisA ? 64 * gw : 0);
-        if (n0 + col < N) {
+          for (int p = 0; p < KS; ++p) {
+            const int g = g0 + 256 * j;
+            w[j][p] = bld16_dev(prs, g < ghi ? (uint32_t)((p * kWgTileFloats + 4 * g) * 4) : kOOB);
+          }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (m0 + row + u < M) C[(m0 + row + u) * N + n0 + col] = scale * v[u];
+        for (int j = 0; j < CPB; ++j) {
+          const int g = g0 + 256 * j;
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < KS; ++p)
+            v += f32x4{__uint_as_float(w[j][p][0]), __uint_as_float(w[j][p][1]), __uint_as_float(w[j][p][2]),
+                       __uint_as_float(w[j][p][3])};
+          const int gl = g & 63, e4 = (g >> 6) & 3, b = (g >> 8) & 1, a = (g >> 9) & 1, gw = g >> 10;
+          const int row = 32 * a + 8 * e4 + 4 * (gl >> 5) + (kYisA ? 0 : 64 * gw);
+          const int col = 32 * b + (gl & 31) + (kYisA ? 64 * gw : 0);
+          if (g < ghi && n0 + col < N) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (m0 + row + u < M) C[(m0 + row + u) * N + n0 + col] = scale * v[u];
+          }
         }
       }
+    }
+  };
+  auto sum_shares = [&](uint32_t mask) __attribute__((always_inline)) {
+    switch (ksplit) {
+      case 2: sum_shares_ks(mask, std::integral_constant<int, 2>{}); break;
+      case 4: sum_shares_ks(mask, std::integral_constant<int, 4>{}); break;
+      case 8: sum_shares_ks(mask, std::integral_constant<int, 8>{}); break;
+      default: sum_shares_ks(mask, std::integral_constant<int, 16>{}); break;
     }
   };
   const uint32_t mine = claim_lds[0];
@@ -504,6 +547,7 @@ int lora_wgrad_ksplit(int64_t D, int64_t R, int64_t T) {
   if (ks > kWgMaxSplit) ks = kWgMaxSplit;
   if (ks < 1) ks = 1;
   if (tiles > kMaxTileCounters) ks = 1;
+  while (ks & (ks - 1)) ks &= ks - 1;  // a power of two (the share sums batch loads by it)
   return (int)ks;
 }
 

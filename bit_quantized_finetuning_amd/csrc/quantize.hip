@@ -7,8 +7,12 @@
 // "메모리 회계"): the block scales are re-coded to 8 bits against their group
 // maximum so that they come back as (q2/256) * S.
 //
-// Workgroups are persistent: each takes groups of 256 blocks (16384 weights)
-// blockIdx.x, blockIdx.x + gridDim.x, ... and builds its search table once.
+// One launch quantizes up to kQuantizeJobs weights (a table of jobs passed as a
+// kernel argument): their groups of 256 blocks (16384 weights) are numbered
+// one after another, and persistent workgroups take groups blockIdx.x,
+// blockIdx.x + gridDim.x, ... of that sequence, so small weights share the
+// launch, its start-up and its tail with the large ones. Each workgroup
+// builds its search table once.
 // Eight lanes share a block: each loads 8 consecutive weights (32 contiguous
 // bytes of float32, the eight lanes together 256 contiguous bytes), the eight
 // reduce the block absmax, and each lane emits its weights' codes as one packed
@@ -36,7 +40,7 @@
 // 2^-100, are recomputed with the IEEE divide. The rule is checked against the
 // plain count on the host, with the quotient perturbed by up to 4 ulp.
 //
-// For absmax-only storage (sshift 0) each block's float32 absmax is written as
+// For absmax-only storage (a job without scale codes) each block's float32 absmax is written as
 // its scale instead, and there is no group step.
 #include "kernels.h"
 
@@ -46,10 +50,7 @@ constexpr int kQTable = 2048;
 constexpr int64_t kQuantizeGrid = 1024;
 
 template <bool kBf16In>
-__global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, int64_t nblocks,
-                                                  uint8_t *__restrict__ codes, uint8_t *__restrict__ qscale,
-                                                  float *__restrict__ smax, uint32_t *__restrict__ flags,
-                                                  int sshift, Nf4Consts c) {
+__global__ __launch_bounds__(256) void k_quantize(QuantizeJobs J, uint32_t *__restrict__ flags, Nf4Consts c) {
   constexpr int esz = kBf16In ? 2 : 4;
   constexpr int kPasses = kGroup / 32;
   __shared__ float s_blk[kGroup];
@@ -59,13 +60,19 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   const int tid = threadIdx.x;
   const int l8 = tid & 7;
   const int slot = tid >> 3;  // 32 blocks per pass
-  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  const int64_t ngroups = J.gstart[J.n];  // groups of all jobs
 
+  // The job holding group g, searched forward from job j (g only grows).
+  auto job_of = [&](int64_t g, int j) {
+    while (j + 1 < J.n && g >= J.gstart[j + 1]) ++j;
+    return j;
+  };
   u32x4 raw[kPasses][kBf16In ? 1 : 2];
-  auto load_group = [&](int64_t g) {
-    const int64_t b0 = g * kGroup;
+  auto load_group = [&](int64_t g, int j) {
+    const int64_t b0 = (g - J.gstart[j]) * kGroup;
+    const int64_t nblocks = J.nblocks[j];
     const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
-    const rsrc_t wr = make_rsrc(static_cast<const uint8_t *>(W) + b0 * kBlock * esz, (int64_t)nb * kBlock * esz);
+    const rsrc_t wr = make_rsrc(static_cast<const uint8_t *>(J.W[j]) + b0 * kBlock * esz, (int64_t)nb * kBlock * esz);
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int b = p * 32 + slot;
@@ -75,7 +82,11 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
     }
   };
   int64_t g = blockIdx.x;
-  if (g < ngroups) load_group(g);
+  int j = 0;
+  if (g < ngroups) {
+    j = job_of(g, 0);
+    load_group(g, j);
+  }
 
   // Bucket b = sign * 32 + e * 4 + m covers magnitudes [lo, hi): e = 0 is
   // [0, 2^-5); e = 1 .. 6 the binade [2^(e-6), 2^(e-5)) cut into quarters by m.
@@ -121,8 +132,14 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
   __syncthreads();
 
   for (; g < ngroups; g += gridDim.x) {
-    const int64_t b0 = g * kGroup;
+    j = job_of(g, j);
+    const int64_t gl = g - J.gstart[j];  // group of job j
+    const int64_t b0 = gl * kGroup;
+    const int64_t nblocks = J.nblocks[j];
     const int nb = (int)(nblocks - b0 < kGroup ? nblocks - b0 : kGroup);
+    uint8_t *const codes = J.codes[j];
+    uint8_t *const qscale = J.qscale[j];
+    float *const smax = J.smax[j];
     uint32_t bad = 0;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -176,11 +193,11 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
         *reinterpret_cast<uint32_t *>(codes + (b0 + b) * (kBlock / 2) + l8 * 4) = word;
       }
     }
-    if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
+    if (g + gridDim.x < ngroups) load_group(g + gridDim.x, job_of(g + gridDim.x, j));
     __syncthreads();
 
     const float s = tid < nb ? s_blk[tid] : 0.f;
-    if (sshift == 0) {  // absmax-only storage: the block scales as they are
+    if (!qscale) {  // absmax-only storage: the block scales as they are
       if (tid < nb) smax[b0 + tid] = s;
     } else {
       float S = s;
@@ -198,7 +215,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *__restrict__ W, in
         }
         qscale[b0 + tid] = (uint8_t)q2;
       }
-      if (tid == 0) smax[g] = S;
+      if (tid == 0) smax[gl] = S;
     }
     if (bad && flags) atomicOr(flags, 1u);
     __syncthreads();  // s_blk and s_red are reused by the next group
@@ -242,19 +259,17 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
   }
 }
 
-hipError_t launch_quantize(const void *W, bool bf16_in, int64_t d_out, int64_t d_in, uint8_t *codes,
-                           uint8_t *qscale, float *smax, uint32_t *flags, const Nf4Consts &c,
+hipError_t launch_quantize(const QuantizeJobs &jobs, bool bf16_in, uint32_t *flags, const Nf4Consts &c,
                            hipStream_t st) {
-  const int64_t nblocks = d_out * d_in / kBlock;
-  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-  const int sshift = qscale ? kDqShift : 0;
+  const int64_t ngroups = jobs.gstart[jobs.n];
+  if (jobs.n < 1 || jobs.n > kQuantizeJobs || ngroups < 1) return hipErrorInvalidValue;
   // persistent workgroups: four per compute unit of a 256-CU part (their LDS
   // allows four), or one per group when there are fewer groups
   const unsigned grid = (unsigned)(ngroups < kQuantizeGrid ? ngroups : kQuantizeGrid);
   if (bf16_in)
-    k_quantize<true><<<dim3(grid), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift, c);
+    k_quantize<true><<<dim3(grid), dim3(256), 0, st>>>(jobs, flags, c);
   else
-    k_quantize<false><<<dim3(grid), dim3(256), 0, st>>>(W, nblocks, codes, qscale, smax, flags, sshift, c);
+    k_quantize<false><<<dim3(grid), dim3(256), 0, st>>>(jobs, flags, c);
   return hipGetLastError();
 }
 

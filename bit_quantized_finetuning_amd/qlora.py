@@ -54,6 +54,8 @@ _W = ctypes.POINTER(_Nf4Weight)
 
 _lib.qlora_quantize.argtypes = [_vp, ctypes.c_int, _W, _vp, _vp]
 _lib.qlora_quantize.restype = ctypes.c_int
+_lib.qlora_quantize_many.argtypes = [ctypes.POINTER(_vp), ctypes.c_int, _W, _i32, _vp, _vp]
+_lib.qlora_quantize_many.restype = ctypes.c_int
 _lib.qlora_dequantize.argtypes = [_W, ctypes.c_int, _vp, _vp]
 _lib.qlora_dequantize.restype = ctypes.c_int
 _lib.qlora_merge.argtypes = [_W, _vp, _vp, _i32, _f32, _vp, _vp]
@@ -288,6 +290,41 @@ def qlora_quantize(W: torch.Tensor, out: NF4Weight | None = None, flags: torch.T
     cw = out._c()
     _check(_lib.qlora_quantize(_ptr(W), dt, ctypes.byref(cw), _ptr(flags), _stream(W.device)), "qlora_quantize")
     return out
+
+
+def qlora_quantize_many(Ws, outs=None, flags: torch.Tensor | None = None,
+                        double_quant: bool = True) -> list:
+    """NF4-quantize several weights of one dtype in shared launches (the results equal one qlora_quantize per
+    weight); `outs` (optional) names each weight's output buffers."""
+    Ws = list(Ws)
+    if not Ws:
+        return []
+    dtypes = {W.dtype for W in Ws}
+    if len(dtypes) != 1 or dtypes.pop() not in (torch.float32, torch.bfloat16):
+        raise TypeError("all weights must be float32, or all bfloat16")
+    dt = F32 if Ws[0].dtype == torch.float32 else BF16
+    if outs is None:
+        outs = [None] * len(Ws)
+    outs = list(outs)
+    if len(outs) != len(Ws):
+        raise ValueError(f"{len(Ws)} weights but {len(outs)} outputs")
+    if flags is not None and (flags.dtype not in (torch.int32, torch.uint32) or flags.numel() < 1):
+        raise TypeError("flags must be a 32-bit integer tensor of at least one element")
+    for i, W in enumerate(Ws):
+        if W.dim() != 2 or not W.is_contiguous():
+            raise ValueError("every W must be a contiguous 2-D tensor")
+        if outs[i] is None:
+            outs[i] = NF4Weight.empty(W.shape[0], W.shape[1], W.device, double_quant)
+        o = outs[i]
+        if (o.d_out, o.d_in) != tuple(W.shape):
+            raise ValueError(f"out {i} is {o.d_out}x{o.d_in}, W is {W.shape[0]}x{W.shape[1]}")
+        _check_weight(o)
+        _check_devices(Ws[0].device, W=W, codes=o.codes, qscale=o.qscale, smax=o.smax, flags=flags)
+    wp = (_vp * len(Ws))(*[W.data_ptr() for W in Ws])
+    cw = (_Nf4Weight * len(Ws))(*[o._c() for o in outs])
+    _check(_lib.qlora_quantize_many(wp, dt, cw, len(Ws), _ptr(flags), _stream(Ws[0].device)),
+           "qlora_quantize_many")
+    return outs
 
 
 def qlora_dequantize(w: NF4Weight, dtype=torch.bfloat16) -> torch.Tensor:

@@ -119,6 +119,21 @@ int qlora_quantize(const void *W, int w_dtype, const qlora_nf4_weight *out, uint
                    hipStream_t stream);
 
 /*
+ * Quantize several weights at once, as a model load does for every projection:
+ * the results are those of `count` qlora_quantize calls (bit for bit), but up
+ * to 32 weights share one launch, so small weights do not each pay a launch
+ * and a partly idle tail.
+ *   W      host array of `count` device pointers, all of dtype w_dtype
+ *   out    host array of `count` structs naming each weight's output buffers
+ *          (double-quant and absmax-only storage may be mixed)
+ *   flags  as for qlora_quantize, shared by all weights
+ * Every job's arguments are checked before anything is launched (an argument
+ * error writes nothing). Errors: as qlora_quantize, and SHAPE for count < 0.
+ */
+int qlora_quantize_many(const void *const *W, int w_dtype, const qlora_nf4_weight *out, int32_t count,
+                        uint32_t *flags, hipStream_t stream);
+
+/*
  * Restore the full weight (for checking, merging or export).
  *   out  device, [d_out, d_in], float32 (the unrounded float32 product) or bf16.
  */

@@ -130,6 +130,22 @@ def test_quantize_and_dequantize_reject_bad_arguments():
     assert q.lib.qlora_dequantize(ctypes.byref(w), 0, BAD, None) == ERR_ALIGN
 
 
+def test_quantize_many_rejects_bad_arguments_before_launching():
+    """A bad job anywhere in the list is found before any launch (here no GPU is there to launch on)."""
+    ws = (q._Nf4Weight * 3)(_w(), _w(), _w(d_in=65))
+    ptrs = (ctypes.c_void_p * 3)(GOOD, GOOD, GOOD)
+    assert q.lib.qlora_quantize_many(ptrs, 0, ws, -1, None, None) == ERR_SHAPE
+    assert q.lib.qlora_quantize_many(None, 0, ws, 2, None, None) == ERR_NULL
+    assert q.lib.qlora_quantize_many(ptrs, 0, None, 2, None, None) == ERR_NULL
+    assert q.lib.qlora_quantize_many(ptrs, 0, ws, 3, None, None) == ERR_SHAPE        # the third job
+    assert q.lib.qlora_quantize_many(ptrs, 7, ws, 2, None, None) == ERR_DTYPE
+    assert q.lib.qlora_quantize_many(ptrs, 0, ws, 0, None, None) == 0                # nothing to do
+    bad = (ctypes.c_void_p * 2)(GOOD, BAD)
+    assert q.lib.qlora_quantize_many(bad, 0, ws, 2, None, None) == ERR_ALIGN
+    nul = (ctypes.c_void_p * 2)(GOOD, None)
+    assert q.lib.qlora_quantize_many(nul, 0, ws, 2, None, None) == ERR_NULL
+
+
 def test_merge_rejects_bad_arguments():
     w = _w()
     assert q.lib.qlora_merge(ctypes.byref(w), GOOD, GOOD, 8, 16.0, None, None) == ERR_NULL

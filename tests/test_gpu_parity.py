@@ -108,6 +108,45 @@ def test_quantize_flags_non_finite():
     assert int(flags.item()) == 0
 
 
+@pytest.mark.parametrize("wdtype", ["bf16", "f32"])
+def test_quantize_many_equals_single_calls(wdtype):
+    """qlora_quantize_many over 37 weights (two launches: 32 jobs, then 5) of mixed shapes, groups that straddle
+    rows, short last groups, both storages mixed, gives the same bits as one qlora_quantize per weight; one
+    weight is also checked against the oracle."""
+    say(f"quantize_many {wdtype}")
+    dt = torch.bfloat16 if wdtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2024)
+    shapes = [(16, 64), (48, 192), (80, 320), (1024, 5120), (5120, 1024), (272, 5120), (32, 5120), (16, 16384)]
+    Ws, dq = [], []
+    for i in range(37):
+        d_out, d_in = shapes[i % len(shapes)]
+        Ws.append((torch.randn(d_out, d_in, device="cuda", generator=gen) * (0.02 * (1 + i % 3))).to(dt))
+        dq.append(i % 5 != 3)  # every fifth weight in absmax-only storage
+    outs = [q.NF4Weight.empty(W.shape[0], W.shape[1], W.device, d) for W, d in zip(Ws, dq)]
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = q.qlora_quantize_many(Ws, outs, flags=flags)
+    ref = [q.qlora_quantize(W, double_quant=d) for W, d in zip(Ws, dq)]
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a.codes, b.codes), f"weight {i}: codes differ"
+        assert (a.qscale is None) == (b.qscale is None)
+        if a.qscale is not None:
+            assert torch.equal(a.qscale, b.qscale), f"weight {i}: scale codes differ"
+        assert torch.equal(a.smax.view(torch.int32), b.smax.view(torch.int32)), f"weight {i}: scales differ"
+    W2 = Ws[2].float().cpu().numpy()
+    codes, q2, S = oracle.quantize(W2)[:3]
+    assert np.array_equal(got[2].codes.cpu().numpy(), codes)
+    assert np.array_equal(got[2].qscale.cpu().numpy(), q2)
+    assert np.array_equal(got[2].smax.cpu().numpy().view(np.uint32), np.asarray(S, dtype=np.float32).view(np.uint32))
+    # a non-finite weight in one job sets the shared flag
+    Ws[30][1, 2] = float("inf")
+    q.qlora_quantize_many(Ws[28:33], flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & 1
+
+
 # ---------------------------------------------------------------------------
 # forward / backward: tolerance
 # ---------------------------------------------------------------------------
