@@ -110,25 +110,33 @@ __global__ __launch_bounds__(256) void k_lora_tall(const uint16_t *__restrict__ 
     wait_barrier<(kAhead - 1) * (2 + NCQ)>();
     copy_step(kk + kAhead < k1 ? kk + kAhead : k1 - 1);  // into the slot step kk-1 used
     const uint8_t *slot = tsm + ((kk - k0) % RS) * kSlot;
+    // Every fragment of the step is read before the first MFMA, so the step
+    // waits for LDS once.
+    u32x4 a[2][4], b[2][kNtw];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4 a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * i + li;
-        a[i] = *reinterpret_cast<const u32x4 *>(slot + row * 128 + (((4 * h + g) ^ qsw(row)) << 4));
+        a[h][i] = *reinterpret_cast<const u32x4 *>(slot + row * 128 + (((4 * h + g) ^ qsw(row)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < kNtw; ++j) {
         const int ct = wave + 4 * j;  // column tile
-        if (ct < nt) {                // wave-uniform
-          const int row = 16 * ct + li;
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(slot + 8192 + row * 128 + (((4 * h + g) ^ qsw(row)) << 4));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(a[i], b, acc[i][j]);
-        }
+        const int row = 16 * ct + li;
+        b[h][j] = ct < nt ? *reinterpret_cast<const u32x4 *>(slot + 8192 + row * 128 + (((4 * h + g) ^ qsw(row)) << 4))
+                          : u32x4{0u, 0u, 0u, 0u};  // (wave-uniform) no such tile
       }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < kNtw; ++j) {
+        if (wave + 4 * j < nt) {  // wave-uniform
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(a[h][i], b[h][j], acc[i][j]);
+        }
+      }
   }
 
   // lane (li, g): tokens 16i + 4g + e of token tile i, column 16 ct + li

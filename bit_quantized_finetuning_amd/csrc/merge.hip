@@ -10,114 +10,118 @@
 // in float32 and rounded once to bf16.
 //
 // The kernel is bound by the bf16 output stream (2 bytes per weight written
-// against 0.52 read), so it is laid out for many independent waves with their
-// loads in flight, and no workgroup-wide step after the start:
-//   * a workgroup owns one strip of 64 columns (one 64-weight block per row)
-//     and 4 x kMgRT row tiles of 32 rows; wave w takes row tiles w, w + 4, ...;
-//   * the strip's slice of A (r rank entries x 64 columns) is staged once in
-//     LDS as it lies in memory, rank-major;
-//   * per row tile a wave issues all its global loads at once, one tile ahead:
-//     B rows (16 bytes per lane and 16 rank entries) and each lane's 16 bytes
-//     of packed codes (half a row of the strip: 32 weights), its block's scale
-//     code and group maximum;
+// against 0.52 read). Workgroups walk along the rows: each owns a band of 128
+// rows and a run of 64-column strips (one 64-weight block per row per strip),
+// so that the loads of the next strip fly while the current one is computed
+// and stored, and every operand that does not change along the band is read
+// once:
+//   * wave w owns rows 32 w .. 32 w + 31 of the band; its slice of B (32 rows
+//     x r) is loaded once into registers as the MFMA's B operand (16 bytes per
+//     lane and 16 rank entries);
+//   * per strip the slice of A (r rank entries x 64 columns, rank-major, as it
+//     lies in memory) goes into one of two LDS buffers; it is loaded into
+//     registers during the previous strip, so one barrier per strip makes it
+//     visible and frees the buffer of the strip before;
+//   * per strip each lane loads 16 bytes of packed codes (half a row of the
+//     strip: 32 weights), its block's scale code and group maximum, also one
+//     strip ahead;
 //   * the product is formed transposed, (s B A)^T = A^T B^T, with
 //     v_mfma_f32_32x32x16_bf16: the A side comes from LDS through
 //     ds_read_b64_tr_b16 (8 consecutive rank entries of one column per lane),
-//     the B rows are the other operand as loaded. Lane l then holds, for row
-//     l % 32 of the tile, runs of 4 consecutive columns; one v_permlane32_swap
-//     per accumulator pair gives lane l all 32 columns 32 (l / 32) .. +31 of
-//     its row -- exactly the weights of its 16 code bytes;
-//   * each lane builds its block's restore table once, restores the 32
-//     weights, adds and rounds into the wave's LDS tile; the tile then goes
-//     out with eight consecutive lanes on each 128-byte row, so every store
-//     instruction writes whole lines (16-byte pieces of 64 different lines ran
-//     at four fifths of the rate).
+//     the B rows are the other operand. Lane l then holds, for row l % 32 of
+//     the wave's rows, runs of 4 consecutive columns; one v_permlane32_swap per
+//     accumulator pair gives lane l all 32 columns 32 (l / 32) .. +31 of its
+//     row -- exactly the weights of its 16 code bytes;
+//   * each lane builds its block's restore table, restores the 32 weights,
+//     adds and rounds into the wave's LDS tile; the tile then goes out with
+//     eight consecutive lanes on each 128-byte row, so every store instruction
+//     writes whole lines.
 #include "kernels.h"
 #include "tiles.h"
 
 namespace qlora {
 
 constexpr int kMgCols = 64;                   // columns (d_in) per strip: one block per row
-constexpr int kMgRows = 32;                   // rows per row tile
+constexpr int kMgRows = 32;                   // rows per wave
 constexpr int kMgWaves = 4;
-constexpr int kMgRT = 2;                      // row tiles per wave
+constexpr int kMgBand = kMgRows * kMgWaves;   // rows per workgroup
 constexpr int kMgAPitch = kMgCols * 2 + 32;   // bytes per staged A row: 4 consecutive rows on distinct banks
 constexpr int kMgOPitch = kMgCols * 2 + 16;   // bytes per row of a wave's output tile in LDS
 constexpr int kMgOBytes = kMgRows * kMgOPitch;
 constexpr int kMgMaxSteps = QLORA_MAX_RANK / 16;
+constexpr int kMgTargetWgs = 1024;            // about four workgroups per CU of a 256-CU part
 
-// LDS for RS rank steps: 16 RS rank rows of A (those from r on are zero), then each wave's output tile
+// LDS for RS rank steps: two buffers of 16 RS rank rows of A (those from r on
+// are zero), then each wave's output tile
 __host__ __device__ constexpr size_t mg_a_bytes(int rs) { return (size_t)(rs > 0 ? 16 * rs : 1) * kMgAPitch; }
-__host__ __device__ constexpr size_t mg_lds(int rs) { return mg_a_bytes(rs) + (size_t)kMgWaves * kMgOBytes; }
+__host__ __device__ constexpr size_t mg_lds(int rs) { return 2 * mg_a_bytes(rs) + (size_t)kMgWaves * kMgOBytes; }
 
 template <int RS>  // rank steps of 16 (r <= 16 RS)
 __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ qscale,
                                                const float *__restrict__ smax, int64_t d_out, int64_t d_in,
                                                const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int r,
                                                float scale, uint16_t *__restrict__ out, int sshift, int strips,
-                                               int groups) {
+                                               int chunk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mg_smem[];
+  constexpr int kAPer = RS > 0 ? (16 * RS * (kMgCols / 8) + 255) / 256 : 1;  // 16-byte A pieces per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ml = lane & 31, half = lane >> 5;
-  uint8_t *o_w = mg_smem + mg_a_bytes(RS) + (size_t)wave * kMgOBytes;
-  // Workgroup -> (strip, row group), XCD-aware: consecutive workgroups go to
-  // the eight XCDs in turn, so XCD x (blockIdx % 8) takes the x-th eighth of
-  // the tiles in the order (line group, row group, strip within the line
-  // group). The four strips of a line group share every 128-byte line of
-  // packed codes (32 bytes each); run on one XCD at about the same time they
-  // read each line from HBM once, through that XCD's L2.
-  const int64_t lgroups = (strips + 3) / 4, ntiles = lgroups * groups * 4;
-  const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t L = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  const int64_t strip = (L / (groups * 4)) * 4 + (L & 3);
-  if (L >= ntiles || strip >= strips) return;  // the whole workgroup, before any barrier
-  const int64_t k0 = strip * kMgCols;
-  const int64_t nbase = ((L >> 2) % groups) * (kMgRows * kMgWaves * kMgRT);
+  uint8_t *o_w = mg_smem + 2 * mg_a_bytes(RS) + (size_t)wave * kMgOBytes;
+  const int64_t nbands = (d_out + kMgBand - 1) / kMgBand;
+  const int64_t band = blockIdx.x % nbands;  // neighbouring workgroups: the same strips of other bands
+  const int s0 = (int)(blockIdx.x / nbands) * chunk;
+  const int s1 = s0 + chunk < strips ? s0 + chunk : strips;
+  if (s0 >= strips) return;  // the whole workgroup, before any barrier
+  const int64_t n0 = band * kMgBand + (int64_t)kMgRows * wave;  // this wave's first row
+  const int64_t rows = n0 >= d_out ? 0 : (d_out - n0 < kMgRows ? d_out - n0 : kMgRows);
+  const bool row_ok = ml < rows;
   const int64_t KB = d_in / kBlock;
   const uint32_t q2o = q2_or(sshift);
 
-  // Loads of row tile t of this wave (rows n0 .. n0 + 31 of the strip).
-  struct TileLoads {
-    u32x4 fb[RS > 0 ? RS : 1];
+  // B slice of this wave: MFMA B operand, column l % 32 (row n0 + l % 32 of B), rank entries
+  // 16 i + 8 (l / 32) .. + 7 (r % 8 == 0: the 8 entries are all in or all out)
+  u32x4 fb[RS > 0 ? RS : 1];
+  if (RS > 0) {
+    const rsrc_t br = make_rsrc(B + n0 * r, rows * r * 2);
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int jb = 16 * i + 8 * half;
+      fb[i] = bld16(br, (row_ok && jb < r) ? (uint32_t)((ml * r + jb) * 2) : kOOB);
+    }
+  }
+  // Per strip: the A slice pieces of this thread (rank row j, columns c8 .. c8 + 7) and this lane's codes.
+  struct StripLoads {
+    u32x4 a[kAPer];
     u32x4 cw;
     uint32_t q2;
     float S;
   };
-  auto tile_row0 = [&](int t) { return nbase + (int64_t)kMgRows * (wave + kMgWaves * t); };
-  auto load_tile = [&](int t, TileLoads &L) {
-    const int64_t n0 = tile_row0(t);
-    const int64_t rows = n0 >= d_out ? 0 : (d_out - n0 < kMgRows ? d_out - n0 : kMgRows);
+  const rsrc_t cr = make_rsrc(codes + n0 * (d_in / 2), rows * (d_in / 2));
+  const rsrc_t ar = make_rsrc(A, (int64_t)r * d_in * 2);  // rank rows r and up read zeros
+  auto load_strip = [&](int s, StripLoads &L) {
+    const int64_t k0 = (int64_t)s * kMgCols;
     if (RS > 0) {
-      const rsrc_t br = make_rsrc(B + n0 * r, rows * r * 2);
 #pragma unroll
-      for (int i = 0; i < RS; ++i) {
-        // MFMA B operand: column l % 32 (row n0 + l % 32 of B), rank entries 16 i + 8 (l / 32) .. + 7
-        // (r % 8 == 0: the 8 entries are all in or all out)
-        const int jb = 16 * i + 8 * half;
-        L.fb[i] = bld16(br, (ml < rows && jb < r) ? (uint32_t)((ml * r + jb) * 2) : kOOB);
+      for (int q = 0; q < kAPer; ++q) {
+        const int e = tid + 256 * q, j = e / (kMgCols / 8), c8 = (e % (kMgCols / 8)) * 8;
+        L.a[q] = bld16(ar, (e < 16 * RS * (kMgCols / 8) && j < r) ? (uint32_t)((j * d_in + k0 + c8) * 2) : kOOB);
       }
     }
     // codes of row n0 + l % 32, columns k0 + 32 (l / 32) .. + 31
-    const rsrc_t cr = make_rsrc(codes + n0 * (d_in / 2), rows * (d_in / 2));
-    L.cw = bld16(cr, ml < rows ? (uint32_t)(ml * (d_in / 2) + k0 / 2 + 16 * half) : kOOB);
+    L.cw = bld16(cr, row_ok ? (uint32_t)(ml * (d_in / 2) + k0 / 2 + 16 * half) : kOOB);
     const int64_t blk = (n0 + ml) * KB + k0 / kBlock;  // the row's block in this strip
-    const bool ok = ml < rows;
-    L.q2 = ok && sshift ? (uint32_t)qscale[blk] : 0u;
-    L.S = ok ? smax[blk >> sshift] : 0.f;
+    L.q2 = row_ok && sshift ? (uint32_t)qscale[blk] : 0u;
+    L.S = row_ok ? smax[blk >> sshift] : 0.f;
+  };
+  auto stage_a = [&](int s, const StripLoads &L) {
+    uint8_t *buf = mg_smem + (s & 1) * mg_a_bytes(RS);
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+      const int e = tid + 256 * q, j = e / (kMgCols / 8), c8 = (e % (kMgCols / 8)) * 8;
+      if (e < 16 * RS * (kMgCols / 8)) st16(buf + j * kMgAPitch + c8 * 2, L.a[q]);
+    }
   };
 
-  TileLoads cur, nxt;
-  load_tile(0, cur);
-
-  // A slice, rank rows 0 .. 16 RS - 1 (zero from r on) x 64 columns, as it lies in memory.
-  if (RS > 0) {
-    for (int e = tid; e < 16 * RS * (kMgCols / 8); e += 256) {
-      const int j = e / (kMgCols / 8), c8 = (e % (kMgCols / 8)) * 8;
-      const u32x4 v = j < r ? *reinterpret_cast<const u32x4 *>(A + (int64_t)j * d_in + k0 + c8) : u32x4{0u, 0u, 0u, 0u};
-      st16(mg_smem + j * kMgAPitch + c8 * 2, v);
-    }
-    __syncthreads();
-  }
   // MFMA A operand from the slice with ds_read_b64_tr_b16: within each 16 lanes,
   // lane u receives element e (e = 0..3) of the 8 bytes that lane 4e + u/4
   // addresses, its 16-bit element u % 4. Lane v of 16-lane group g therefore
@@ -126,18 +130,24 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
   // l % 32, and rank entries 8 (l / 32) .. + 7 over the two reads.
   const int grp = lane >> 4, u16 = lane & 15;
   const uint32_t aoff = (uint32_t)((8 * (grp >> 1) + (u16 >> 2)) * kMgAPitch + (16 * (grp & 1) + 4 * (u16 & 3)) * 2);
-  auto frag_a = [&](int i, int jb) {
-    const uint8_t *p = mg_smem + aoff + 16 * i * kMgAPitch + 64 * jb;
+  auto frag_a = [&](const uint8_t *buf, int i, int jb) {
+    const uint8_t *p = buf + aoff + 16 * i * kMgAPitch + 64 * jb;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * kMgAPitch));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   };
 
-  for (int t = 0; t < kMgRT; ++t) {
-    const int64_t n0 = tile_row0(t);
-    if (n0 >= d_out) break;  // wave-uniform
-    if (t + 1 < kMgRT && tile_row0(t + 1) < d_out) load_tile(t + 1, nxt);
+  StripLoads cur, nxt;
+  load_strip(s0, cur);
+  for (int s = s0; s < s1; ++s) {
+    stage_a(s, cur);
+    // A of strip s is visible; every wave is done with strip s - 1 (its buffer
+    // takes strip s + 1) and with the output tile of strip s - 1.
+    __syncthreads();
+    if (s + 1 < s1) load_strip(s + 1, nxt);
+    const uint8_t *buf = mg_smem + (s & 1) * mg_a_bytes(RS);
+    const int64_t k0 = (int64_t)s * kMgCols;
 
     f32x16 acc[2];
 #pragma unroll
@@ -147,9 +157,9 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
 #pragma unroll
     for (int i = 0; i < RS; ++i)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) acc[jb] = mfma32(frag_a(i, jb), cur.fb[i], acc[jb]);
+      for (int jb = 0; jb < 2; ++jb) acc[jb] = mfma32(frag_a(buf, i, jb), fb[i], acc[jb]);
     // Lane l, accumulator e of column block jb holds strip column 32 jb + 8 (e / 4) + 4 (l / 32) + e % 4 of
-    // tile row l % 32. The swap hands lanes 0..31 the block-0 runs of lanes 32..63 (in acc[1]) and lanes 32..63
+    // row l % 32. The swap hands lanes 0..31 the block-0 runs of lanes 32..63 (in acc[1]) and lanes 32..63
     // the block-1 runs of lanes 0..31 (in acc[0]): lane l then holds columns 32 (l / 32) + 8 k + 0..3 in
     // acc[0][4k .. 4k+3] and + 4..7 in acc[1][4k .. 4k+3].
     uint32_t d0[16], d1[16];
@@ -162,21 +172,21 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
     }
 
     // Restore, add and round into the wave's LDS tile (row-major, 32 rows x 128 bytes), then store it so that
-    // eight consecutive lanes write one whole 128-byte row: the lines go out whole instead of in 16-byte pieces.
+    // eight consecutive lanes write one whole 128-byte row.
     {
       const Nf4Planes tab = make_planes(restore_scale(cur.q2 | q2o, cur.S));
       uint8_t *rowp = o_w + ml * kMgOPitch + 64 * half;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x4 wh = expand8(tab, cur.cw[k]);  // 8 restored weights, element order
-        const float s0 = scale * __uint_as_float(d0[4 * k]), s1 = scale * __uint_as_float(d0[4 * k + 1]);
-        const float s2 = scale * __uint_as_float(d0[4 * k + 2]), s3 = scale * __uint_as_float(d0[4 * k + 3]);
-        const float s4 = scale * __uint_as_float(d1[4 * k]), s5 = scale * __uint_as_float(d1[4 * k + 1]);
-        const float s6 = scale * __uint_as_float(d1[4 * k + 2]), s7 = scale * __uint_as_float(d1[4 * k + 3]);
-        const u32x4 o = {pack_bf16x2(bf16_lo_to_f32(wh[0]) + s0, bf16_hi_to_f32(wh[0]) + s1),
-                         pack_bf16x2(bf16_lo_to_f32(wh[1]) + s2, bf16_hi_to_f32(wh[1]) + s3),
-                         pack_bf16x2(bf16_lo_to_f32(wh[2]) + s4, bf16_hi_to_f32(wh[2]) + s5),
-                         pack_bf16x2(bf16_lo_to_f32(wh[3]) + s6, bf16_hi_to_f32(wh[3]) + s7)};
+        const float t0 = scale * __uint_as_float(d0[4 * k]), t1 = scale * __uint_as_float(d0[4 * k + 1]);
+        const float t2 = scale * __uint_as_float(d0[4 * k + 2]), t3 = scale * __uint_as_float(d0[4 * k + 3]);
+        const float t4 = scale * __uint_as_float(d1[4 * k]), t5 = scale * __uint_as_float(d1[4 * k + 1]);
+        const float t6 = scale * __uint_as_float(d1[4 * k + 2]), t7 = scale * __uint_as_float(d1[4 * k + 3]);
+        const u32x4 o = {pack_bf16x2(bf16_lo_to_f32(wh[0]) + t0, bf16_hi_to_f32(wh[0]) + t1),
+                         pack_bf16x2(bf16_lo_to_f32(wh[1]) + t2, bf16_hi_to_f32(wh[1]) + t3),
+                         pack_bf16x2(bf16_lo_to_f32(wh[2]) + t4, bf16_hi_to_f32(wh[2]) + t5),
+                         pack_bf16x2(bf16_lo_to_f32(wh[3]) + t6, bf16_hi_to_f32(wh[3]) + t7)};
         st16(rowp + 16 * k, o);
       }
     }
@@ -187,13 +197,10 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
     for (int k = 0; k < 4; ++k) {
       const int rr = 8 * k + (lane >> 3), ch = lane & 7;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(o_w + rr * kMgOPitch + 16 * ch);
-      if (n0 + rr < d_out) st16(out + (n0 + rr) * d_in + k0 + 8 * ch, v);
+      if (rr < rows) st16(out + (n0 + rr) * d_in + k0 + 8 * ch, v);
     }
-    // the next tile's writes into the LDS tile come after every lane's reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     cur = nxt;
+    // (the next strip's writes into the output tile come after its barrier)
   }
 }
 
@@ -217,15 +224,20 @@ hipError_t launch_merge(const uint8_t *codes, const uint8_t *qscale, const float
   });
   if (e != hipSuccess) return e;
   const int strips = (int)(d_in / kMgCols);
-  const int64_t rows_per_wg = (int64_t)kMgRows * kMgWaves * kMgRT;
-  const int64_t groups = (d_out + rows_per_wg - 1) / rows_per_wg;
-  const int64_t ntiles = (strips + 3) / 4 * groups * 4;
-  const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));
+  const int64_t nbands = (d_out + kMgBand - 1) / kMgBand;
+  // strips per workgroup: enough workgroups for about four per CU, runs of
+  // four strips (whole 128-byte lines of codes), at least four
+  int64_t chunk = (nbands * strips + kMgTargetWgs - 1) / kMgTargetWgs;
+  chunk = (chunk + 3) / 4 * 4;
+  if (chunk < 4) chunk = 4;
+  if (chunk > strips) chunk = strips;
+  const int64_t nchunks = (strips + chunk - 1) / chunk;
+  const dim3 grid((unsigned)(nbands * nchunks));
   const int sshift = qscale ? kDqShift : 0;
   const int steps = (r + 15) / 16;
 #define QLORA_MERGE_LAUNCH(RS)                                                                                     \
   k_merge<RS><<<grid, dim3(256), mg_lds(RS), st>>>(codes, qscale, smax, d_out, d_in, A, B, r, scale, out, \
-                                                         sshift, strips, (int)groups)
+                                                         sshift, strips, (int)chunk)
   if (steps == 0)
     QLORA_MERGE_LAUNCH(0);
   else if (steps == 1)
