@@ -32,8 +32,9 @@
 //     the wave's rows, runs of 4 consecutive columns; one v_permlane32_swap per
 //     accumulator pair gives lane l all 32 columns 32 (l / 32) .. +31 of its
 //     row -- exactly the weights of its 16 code bytes;
-//   * each lane builds its block's restore table, restores the 32 weights,
-//     adds and rounds into the wave's LDS tile; the tile then goes out with
+//   * each lane builds its block's restore table, restores the 32 weights
+//     straight to float32, adds s (B A) with one fused multiply-add and
+//     rounds into the wave's LDS tile; the tile then goes out with
 //     eight consecutive lanes on each 128-byte row, so every store instruction
 //     writes whole lines.
 #include "kernels.h"
@@ -172,21 +173,29 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t *__restrict__ codes
     }
 
     // Restore, add and round into the wave's LDS tile (row-major, 32 rows x 128 bytes), then store it so that
-    // eight consecutive lanes write one whole 128-byte row.
+    // eight consecutive lanes write one whole 128-byte row. The restore stops at the byte-plane lookups: one
+    // more byte select per weight puts its low and high bf16 bytes into the top half of a zero word, which is
+    // the restored weight as a float32, and one fused multiply-add forms w_hat + s (B A).
     {
       const Nf4Planes tab = make_planes(restore_scale(cur.q2 | q2o, cur.S));
       uint8_t *rowp = o_w + ml * kMgOPitch + 64 * half;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const u32x4 wh = expand8(tab, cur.cw[k]);  // 8 restored weights, element order
-        const float t0 = scale * __uint_as_float(d0[4 * k]), t1 = scale * __uint_as_float(d0[4 * k + 1]);
-        const float t2 = scale * __uint_as_float(d0[4 * k + 2]), t3 = scale * __uint_as_float(d0[4 * k + 3]);
-        const float t4 = scale * __uint_as_float(d1[4 * k]), t5 = scale * __uint_as_float(d1[4 * k + 1]);
-        const float t6 = scale * __uint_as_float(d1[4 * k + 2]), t7 = scale * __uint_as_float(d1[4 * k + 3]);
-        const u32x4 o = {pack_bf16x2(bf16_lo_to_f32(wh[0]) + t0, bf16_hi_to_f32(wh[0]) + t1),
-                         pack_bf16x2(bf16_lo_to_f32(wh[1]) + t2, bf16_hi_to_f32(wh[1]) + t3),
-                         pack_bf16x2(bf16_lo_to_f32(wh[2]) + t4, bf16_hi_to_f32(wh[2]) + t5),
-                         pack_bf16x2(bf16_lo_to_f32(wh[3]) + t6, bf16_hi_to_f32(wh[3]) + t7)};
+        const uint32_t c = cur.cw[k];
+        const uint32_t sa = c & 0x07070707u, ma = ((c >> 1) & 0x04040404u) | 0x03020100u;
+        const uint32_t sb = (c >> 4) & 0x07070707u, mb = ((c >> 5) & 0x04040404u) | 0x03020100u;
+        const uint32_t lo_a = lookup4(tab.lo, sa, ma), hi_a = lookup4(tab.hi, sa, ma);  // e0..e3
+        const uint32_t lo_b = lookup4(tab.lo, sb, mb), hi_b = lookup4(tab.hi, sb, mb);  // e4..e7
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // bytes 0, 1 zero (selector 12), byte 2 the low and byte 3 the high byte of weight e
+          const uint32_t sel = 0x00000c0cu | ((uint32_t)e << 16) | ((uint32_t)(4 + e) << 24);
+          v[e] = fmaf(scale, __uint_as_float(d0[4 * k + e]), __uint_as_float(perm(hi_a, lo_a, sel)));
+          v[4 + e] = fmaf(scale, __uint_as_float(d1[4 * k + e]), __uint_as_float(perm(hi_b, lo_b, sel)));
+        }
+        const u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7])};
         st16(rowp + 16 * k, o);
       }
     }

@@ -147,11 +147,12 @@ int qlora_dequantize(const qlora_nf4_weight *W, int out_dtype, void *out, hipStr
  *   A    device bf16 [r, d_in], B device bf16 [d_out, r]; r = 0 or A = B = NULL
  *        gives the plain bf16 restore
  *   out  device bf16 [d_out, d_in], written in full; 16-byte aligned
- * out = bf16( w_hat + fl32(s * (B A)) ) with s = alpha / r in float32, B A
- * accumulated in float32 and one round-to-nearest-even at the end: within one
- * bf16 unit in the last place of the exactly rounded merge, plus the float32
- * error of forming the sum (2^-24 (|w_hat| + (r+2) s sum_j |B_j||A_j|), which
- * matters only where w_hat and s B A nearly cancel). The weight buffers are
+ * out = bf16( fl32(w_hat + s * (B A)) ) with s = alpha / r in float32, B A
+ * accumulated in float32, s (B A) + w_hat formed by one fused multiply-add and
+ * one round-to-nearest-even to bf16 at the end: within one bf16 unit in the
+ * last place of the exactly rounded merge, plus the float32 error of forming
+ * the sum (2^-24 (|w_hat| + (r+2) s sum_j |B_j||A_j|), which matters only
+ * where w_hat and s B A nearly cancel). The weight buffers are
  * only read. Errors: NULL, SHAPE (r outside 0..256 or r % 8 != 0), ALIGN,
  * HIP (launch failure); nothing is written on a validation error.
  */
