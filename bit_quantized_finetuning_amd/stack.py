@@ -32,8 +32,8 @@ HEAD = 128
 
 
 def rms_norm(x: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
-    xf = x.float()
-    return (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)).to(torch.bfloat16)
+    """x / sqrt(mean(x^2) + eps) over the last dimension, bf16 in and out (torch's fused norm)."""
+    return F.rms_norm(x, (x.shape[-1],), eps=eps)
 
 
 class DecoderProjections(torch.nn.Module):
@@ -52,19 +52,18 @@ class DecoderProjections(torch.nn.Module):
         self.gate_up = QLoRAFusedLinear([weights["gate"], weights["up"]], r=0)
         self.down = QLoRALinear(weights["down"], r=0)
 
-    def _expand(self, t: torch.Tensor) -> torch.Tensor:
-        """[T, kv] -> [T, hidden]: each KV head serves hidden / kv query heads."""
-        T, kvh = t.shape[0], self.kv // self.head
-        rep = self.hidden // self.kv
-        return t.view(T, kvh, 1, self.head).expand(T, kvh, rep, self.head).reshape(T, self.hidden)
+    def _heads(self, t: torch.Tensor, rep: int) -> torch.Tensor:
+        """[T, n * head] -> [T, kv heads, rep, head] (a view; k and v broadcast over the query heads they serve)."""
+        return t.view(t.shape[0], self.kv // self.head, rep, self.head)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         q, k, v = self.qkv(rms_norm(x))
-        a = (q.float() * torch.sigmoid(self._expand(k).float()) + self._expand(v).float()).to(torch.bfloat16)
-        x1 = x + self.o(a)
+        rep = self.hidden // self.kv  # query heads per KV head
+        # a = q * sigmoid(k) + v with k and v broadcast to the query heads (one bf16 rounding, float32 inside)
+        a = torch.addcmul(self._heads(v, 1), self._heads(q, rep), torch.sigmoid(self._heads(k, 1)))
+        x1 = x + self.o(a.reshape(x.shape[0], self.hidden))
         g, u = self.gate_up(rms_norm(x1))
-        m = (F.silu(g.float()) * u.float()).to(torch.bfloat16)
-        return x1 + self.down(m)
+        return x1 + self.down(F.silu(g) * u)
 
 
 class DecoderStack(torch.nn.Module):
