@@ -163,6 +163,40 @@ struct TableBuild {
   }
 };
 
+// The same table build cut into 7 pieces of 4 to 6 VALU instructions: the
+// restored scale, two pairs of level products each (4), the low planes, the
+// high planes.
+struct TableBuild7 {
+  float sh;
+  uint32_t p[8];
+  __device__ __forceinline__ void run(int k, uint32_t q2, uint32_t q2o, float S, Nf4Planes &t) {
+    if (k == 0) {
+      pin(q2);
+      pin(S);
+      sh = restore_scale(q2 | q2o, S);
+      pin(sh);
+    } else if (k <= 4) {
+#pragma unroll
+      for (int u = 2 * (k - 1); u < 2 * k; ++u) {
+        p[u] = pack_bf16x2(code_times(2 * u, sh), code_times(2 * u + 1, sh));
+        pin(p[u]);
+      }
+    } else if (k == 5) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        t.lo[u] = perm(p[2 * u + 1], p[2 * u], 0x06040200u);
+        pin(t.lo[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        t.hi[u] = perm(p[2 * u + 1], p[2 * u], 0x07050301u);
+        pin(t.hi[u]);
+      }
+    }
+  }
+};
+
 // expand8 cut into 4 pieces: selectors, low-plane lookups, high-plane
 // lookups, interleave (the result is complete after piece 3).
 struct Expand {
@@ -187,6 +221,52 @@ struct Expand {
       lo_b = lookup4(t.lo, sb, mb);
       hi_b = lookup4(t.hi, sb, mb);
       pin(lo_b);
+      pin(hi_b);
+    } else {
+      out[0] = perm(hi_a, lo_a, 0x05010400u);
+      out[1] = perm(hi_a, lo_a, 0x07030602u);
+      out[2] = perm(hi_b, lo_b, 0x05010400u);
+      out[3] = perm(hi_b, lo_b, 0x07030602u);
+      pin(out);
+    }
+  }
+};
+
+// expand8 cut into 8 pieces of 3 or 4 VALU instructions each, so that every
+// MFMA of a slice carries at most about four (a single wave co-issues that
+// many with a 32-cycle MFMA for free; one piece of 9 stalls the next MFMA):
+// selectors (3 pieces), the four plane lookups, the interleave.
+struct Expand8 {
+  // (the code word is kept as pinned in piece 0: pure arithmetic on the loaded
+  // word would otherwise drift up to the load's wait, all pieces at once)
+  uint32_t c, x, sa, ma, sb, mb, lo_a, hi_a, lo_b, hi_b;
+  __device__ __forceinline__ void run(int ph, const Nf4Planes &t, uint32_t w, u32x4 &out) {
+    if (ph == 0) {
+      c = w;
+      pin(c);
+      sa = c & 0x07070707u;
+      x = (c >> 1) & 0x04040404u;
+      pin(sa);
+      pin(x);
+    } else if (ph == 1) {
+      ma = x | 0x03020100u;
+      sb = (c >> 4) & 0x07070707u;
+      pin(ma);
+      pin(sb);
+    } else if (ph == 2) {
+      mb = ((c >> 5) & 0x04040404u) | 0x03020100u;
+      pin(mb);
+    } else if (ph == 3) {
+      lo_a = lookup4(t.lo, sa, ma);
+      pin(lo_a);
+    } else if (ph == 4) {
+      hi_a = lookup4(t.hi, sa, ma);
+      pin(hi_a);
+    } else if (ph == 5) {
+      lo_b = lookup4(t.lo, sb, mb);
+      pin(lo_b);
+    } else if (ph == 6) {
+      hi_b = lookup4(t.hi, sb, mb);
       pin(hi_b);
     } else {
       out[0] = perm(hi_a, lo_a, 0x05010400u);
@@ -521,7 +601,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
   // One K step. Tile kt is in ring slot P = kt & 1, its codes in Ccur; Cnext
   // holds the codes of step kt+1. Side work after MFMA q of slice s:
   //   s < 3 : A fragments of slice s+1 (q < 8); B fragments of slice s+1
-  //           (expand pieces at odd q: column tile 0 at q = 1..7, 1 at 9..15);
+  //           (one of 8 expand pieces after every MFMA: column tile 0 at
+  //           q = 0..7, 1 at 8..15);
   //   s = 3 : codes of step kt+2 into Ccur (q = 0); this lane's table of
   //           step kt+1 (q = 1..3) and the swap that shares it (q = 4, 5);
   //           wait for tile kt+1 and barrier (q = 7); then the A and B
@@ -530,8 +611,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
     // (the last step copies its own tile again into the idle slot: no branch)
     dma_tile(xr, xo, (kt + 1 < k1 ? kt + 1 : kt) * kBK, smem + (P ^ 1) * kTile, wave);
     const uint8_t *cur = smem + P * kTile, *nxt = smem + (P ^ 1) * kTile;
-    Expand ex;
-    TableBuild tb;
+    Expand8 ex;
+    TableBuild7 tb;
     Nf4Planes own;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -542,19 +623,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fwd(const uint8_t *__restrict
         QLORA_SCHED_FENCE();
         if (s < 3) {
           if (q < 8) fa[(s + 1) & 1][q] = *reinterpret_cast<const u32x4 *>(cur + aoff[s + 1] + 4096 * q);
-          if (q & 1) {
-            const int jj = q >> 3, ph = (q >> 1) & 3;
-            ex.run(ph, t[jj], Ccur.c[jj][s + 1], fb[(s + 1) & 1][jj]);
-          }
+          const int jj = q >> 3;
+          ex.run(q & 7, t[jj], Ccur.c[jj][s + 1], fb[(s + 1) & 1][jj]);
         } else {
           if (q == 0) issue_codes(kt + 2, Ccur);
-          if (q >= 1 && q <= 3) tb.run(q - 1, Cnext.q2, q2o, Cnext.S, own);
-          if (q == 4 || q == 5) share_tables(own, t, 4 * (q - 4));
+          if (q <= 6) tb.run(q, Cnext.q2, q2o, Cnext.S, own);
+          if (q == 6 || q == 7) share_tables(own, t, 4 * (q - 6));
           if (q == 7) wait_barrier<4>();
           if (q >= 8) {
             fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
-            const int jj = (q - 8) >> 2, ph = (q - 8) & 3;
+            const int jj = (q - 8) >> 2, ph = 2 * ((q - 8) & 3);
             ex.run(ph, t[jj], Cnext.c[jj][0], fb[0][jj]);
+            ex.run(ph + 1, t[jj], Cnext.c[jj][0], fb[0][jj]);
           }
         }
         QLORA_SCHED_FENCE();
@@ -616,18 +696,51 @@ struct DxCodes {
 // Word m of the block goes to byte (wxor ^ 16 m) of the tile: the block's
 // chunks are 8 consecutive positions whose order the swizzle permutes.
 struct DxRestore {
-  TableBuild tb;
+  // 7 table pieces, then 6 pieces per code word (the selectors in two, the
+  // low and high lookups of e0..e3 one each, those of e4..e7 together, the
+  // interleave with the store), one per slot: after each MFMA of slices 0..2
+  // and of slice 3 before its barrier.
+  static constexpr int kPieces = 7 + 8 * 6;
+  TableBuild7 tb;
   Nf4Planes t;
-  Expand ex;
-  u32x4 v;
+  uint32_t w, sa, ma, sb, mb, lo_a, hi_a, lo_b, hi_b;  // w: the word as pinned in its piece 0
   __device__ __forceinline__ void run(int k, const DxCodes &C, uint8_t *tile, uint32_t wxor, uint32_t q2o) {
-    if (k < 3) {
+    if (k < 7) {
       tb.run(k, C.q2, q2o, C.S, t);
-    } else if (k < 35) {
-      const int m = (k - 3) >> 2, ph = (k - 3) & 3;
-      const uint32_t w = m < 4 ? C.c0[m & 3] : C.c1[m & 3];
-      ex.run(ph, t, w, v);
-      if (ph == 3) st16(tile + (wxor ^ (16u * m)), v);
+      return;
+    }
+    if (k >= kPieces) return;
+    const int m = (k - 7) / 6, ph = (k - 7) % 6;
+    if (ph == 0) {
+      w = m < 4 ? C.c0[m & 3] : C.c1[m & 3];
+      pin(w);
+      sa = w & 0x07070707u;
+      ma = ((w >> 1) & 0x04040404u) | 0x03020100u;
+      pin(sa);
+      pin(ma);
+    } else if (ph == 1) {
+      sb = (w >> 4) & 0x07070707u;
+      mb = ((w >> 5) & 0x04040404u) | 0x03020100u;
+      pin(sb);
+      pin(mb);
+    } else if (ph == 2) {
+      lo_a = lookup4(t.lo, sa, ma);
+      pin(lo_a);
+    } else if (ph == 3) {
+      hi_a = lookup4(t.hi, sa, ma);
+      pin(hi_a);
+    } else if (ph == 4) {
+      lo_b = lookup4(t.lo, sb, mb);
+      hi_b = lookup4(t.hi, sb, mb);
+      pin(lo_b);
+      pin(hi_b);
+    } else {
+      u32x4 v;
+      v[0] = perm(hi_a, lo_a, 0x05010400u);
+      v[1] = perm(hi_a, lo_a, 0x07030602u);
+      v[2] = perm(hi_b, lo_b, 0x05010400u);
+      v[3] = perm(hi_b, lo_b, 0x07030602u);
+      st16(tile + (wxor ^ (16u * m)), v);
     }
   }
 };
@@ -723,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   {
     DxRestore rs;
 #pragma unroll
-    for (int k = 0; k < 35; ++k) rs.run(k, C0, Bt, wxor, q2o);
+    for (int k = 0; k < DxRestore::kPieces; ++k) rs.run(k, C0, Bt, wxor, q2o);
   }
   wait_barrier<4>();
 #pragma unroll
@@ -735,8 +848,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
   // kt+1, whose weight tile is restored into slot P^1 during this step; Ccur
   // (dead) receives the codes of step kt+2. Side work after MFMA q of slice s:
   //   s < 3 : A fragments of slice s+1 (q < 8), B fragments (q = 8, 10);
-  //           restore pieces 16s + q (all 35 done within slice 2);
-  //   s = 3 : wait for the copies and stores of step kt+1 and barrier (q = 7);
+  //           restore piece 16s + q (55 pieces: slices 0..2 and slice 3 up to q = 6);
+  //   s = 3 : restore pieces 48 + q (q < 7); wait for the copies and stores
+  //           of step kt+1 and barrier (q = 7);
   //           A and B fragments of step kt+1, slice 0 (q = 8..15).
   auto step = [&](int kt, const int P, DxCodes &Ccur, DxCodes &Cnext) {
     wait_vmem();  // codes of step kt+1 (requested a step ago) are in; see dma16_asm
@@ -758,6 +872,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dx(const uint8_t *__restrict_
           if (q == 8 || q == 10) fb[(s + 1) & 1][(q - 8) >> 1] = frag_b(bcur, s + 1, (q - 8) >> 1);
           rs.run(16 * s + q, Cnext, bnxt, wxor, q2o);
         } else {
+          if (q < 7) rs.run(48 + q, Cnext, bnxt, wxor, q2o);
           if (q == 7) wait_barrier<4>();
           if (q >= 8) fa[0][q - 8] = *reinterpret_cast<const u32x4 *>(nxt + aoff[0] + 4096 * (q - 8));
           if (q == 12 || q == 14) fb[0][(q - 12) >> 1] = frag_b(bnxt, 0, (q - 12) >> 1);
