@@ -238,7 +238,9 @@ def bench_train(args, torch, q, synth, dev, wname):
     # the fused dequant-GEMM + LoRA forward: algorithmic flops of all forward calls over their summed duration
     fwd_tf = ff / (sum(fwd_ms) * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(FWD_TRAFFIC_RECORD),
+            "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4),
+            # the recorded counters are those of this call on the 65B layer with double-quant storage
+            "traffic": recorded_traffic(FWD_TRAFFIC_RECORD) if wname == "65b_layer" and not ABSMAX_STORAGE[0] else None,
             "kernel": "qlora_forward at T = %d: k_lora_tall (u = x A^T) then k_gemm_fwd (dequant GEMM with the "
                       "adapter term as extra K columns)" % T if T >= 65 else "qlora_forward",
             "flops_per_launch": round(ff / n), "us_per_launch": round(1e3 * sum(fwd_ms) / n, 2),
@@ -637,7 +639,7 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
         achieved = (fb / len(calls)) / (us_launch * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic() if wname == "llama7b_skinny" else None,
+                "traffic": recorded_traffic() if wname == "llama7b_skinny" and not ABSMAX_STORAGE[0] else None,
                 "kernel": "k_gemv_fwd (qlora_forward, T <= 16)",
                 "bytes_per_launch": round(fb / len(calls)), "us_per_launch": round(us_launch, 3),
                 "launches": launches}
