@@ -293,7 +293,7 @@ def bench_train(args, torch, q, synth, dev, wname):
         sk = bench_graph(sargs, torch, q, synth, dev, "llama7b_skinny", emit=False)
         line["skinny"] = {"workload": sk["config"]["workload"], "value": sk["value"], "unit": sk["unit"],
                           "ms_per_step": sk["ms_per_step"], "steps": sargs.steps, "roofline": sk["roofline"],
-                          "per_call": sk["per_call"]}
+                          "per_call": sk["per_call"], "grouped": sk.get("grouped")}
         print("[bench] skinny record done", file=sys.stderr, flush=True)
         line["hbm_ceiling"] = hbm_ceiling(torch, dev)
     print(json.dumps(line), flush=True)
@@ -650,6 +650,8 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
                 "kernel": "whole forward + backward step (all kernels)"}
 
     per_call = per_call_times(torch, dev, calls, run_call, chunk) if not (args.no_graph or args.no_per_call) else []
+    grouped = (grouped_times(torch, dev, q, calls, nT, chunk, args.steps, fb, wbytes_step)
+               if not (bw or args.no_graph) else None)
 
     if args.copy_calibration:
         copy_calibration(torch, dev)
@@ -684,6 +686,7 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
         "total_GBs": round((fb + bb) / (ms_step * 1e-3) / 1e9, 1),
         "roofline": roof,
         "per_call": per_call,
+        **({"grouped": grouped} if grouped else {}),
         "cpu_baseline": cpu,
     }
     if paged_info:
@@ -713,6 +716,29 @@ def recorded_traffic(record=TRAFFIC_RECORD):
         return int(rec["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def grouped_times(torch, dev, q, calls, nT, chunk, steps, fb_step, wbytes_step):
+    """The same step with its calls, which are independent, given to qlora_forward_many: one launch per step
+    when they share a kernel variant. Graph-timed like the step, on the same rotating weight copies and inputs."""
+    ws = torch.zeros(q.qlora_forward_many_workspace_bytes(len(calls)), dtype=torch.uint8, device=dev)
+
+    def body(s):
+        jobs = []
+        for p, copies, x, dy, h, g, T, ti in calls:
+            wc, A, B = copies[(s * nT + ti) % len(copies)]
+            jobs.append({"w": wc, "x": x, "A": A, "B": B, "alpha": p.alpha, "h": h})
+        q.qlora_forward_many(jobs, ws=ws)
+
+    ms, n = _timed_graph(torch, dev, body, steps, chunk)
+    achieved = fb_step / (ms * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 5), "steps": n, "weight_GBs": round(wbytes_step / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": ("k_gemv_fwd_many (qlora_forward_many: one launch per kernel variant among "
+                                    "the step's calls)"),
+                         "bytes_per_step": round(fb_step), "us_per_step": round(ms * 1e3, 3)},
+            "fallbacks": q.qlora_workspace_fallbacks(ws)}
 
 
 def per_call_times(torch, dev, calls, run_call, chunk):

@@ -441,6 +441,41 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
   return enqueue_forward(W, x, T, A, B, r, alpha, h, u_out, ws, stream);
 }
 
+// qlora_forward_many's workspace: the counter region, then one tagged exchange
+// buffer per job, sized for the largest rank (4 K slices x 16 tokens x r_pad
+// tagged float32 partials of u).
+constexpr size_t kUexJobBytes = (size_t)4 * 16 * QLORA_MAX_RANK * 8;
+static size_t many_uex_offset() { return align256((size_t)kMaxCounters * sizeof(uint32_t)); }
+
+size_t qlora_forward_many_workspace_bytes(int32_t count) {
+  if (count < 1 || count > QLORA_MAX_FORWARD_JOBS) return 0;
+  return many_uex_offset() + (size_t)count * kUexJobBytes;
+}
+
+int qlora_forward_many(const qlora_forward_job *jobs, int32_t count, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (!jobs) return QLORA_ERR_NULL;
+  if (count < 1 || count > QLORA_MAX_FORWARD_JOBS) return QLORA_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const qlora_forward_job &j = jobs[i];
+    const int s = validate_forward(j.W, j.x, j.T, j.A, j.B, j.r, j.h, j.u_out);
+    if (s) return s;
+    if (j.T > 16 || !gemv_supported(j.W->d_out, j.W->d_in, j.T)) return QLORA_ERR_SHAPE;
+  }
+  if (ws_bytes < qlora_forward_many_workspace_bytes(count)) return QLORA_ERR_WORKSPACE;
+  if (!ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  GemvJob g[QLORA_MAX_FORWARD_JOBS];
+  for (int i = 0; i < count; ++i) {
+    const qlora_forward_job &j = jobs[i];
+    const int r = j.A || j.B ? j.r : 0;
+    g[i] = GemvJob{j.W->codes, j.W->qscale, j.W->smax, j.W->d_out, j.W->d_in, j.x, j.T, j.A, j.B, r, rank_pad(r),
+                   r > 0 ? j.alpha / (float)r : 0.f, j.h, j.u_out,
+                   at<uint64_t>(ws, many_uex_offset() + (size_t)i * kUexJobBytes)};
+  }
+  return hip_status(launch_gemv_fwd_many(g, count, at<uint32_t>(ws, (kMaxCounters - kSyncWords) * 4), stream));
+}
+
 int qlora_backward(const qlora_nf4_weight *W, const uint16_t *x, const uint16_t *dY, int64_t T, const uint16_t *A,
                    const uint16_t *B, int32_t r, float alpha, const float *u_saved, uint16_t *dX, float *dA,
                    float *dB, void *ws, size_t ws_bytes, hipStream_t stream) {

@@ -98,6 +98,40 @@ hipError_t launch_gemv_fwd(const uint8_t *codes, const uint8_t *qscale, const fl
                            hipStream_t st);
 // Whether the T <= 16 kernel takes these sizes (its buffer ranges cover whole tensors).
 bool gemv_supported(int64_t d_out, int64_t d_in, int64_t T);
+// Several independent T <= 16 forwards (launch_gemv_fwd's arguments, each with
+// its own exchange buffer uex) in as few launches as their kernel variants
+// allow; the status words `sync` are shared. The kernel argument of one launch:
+// job j runs on workgroups wg0[j] .. wg0[j+1]-1.
+struct GemvJob {
+  const uint8_t *codes, *qscale;
+  const float *smax;
+  int64_t d_out, d_in;
+  const uint16_t *x;
+  int64_t T;
+  const uint16_t *A, *B;
+  int r, r_pad;
+  float scale;
+  uint16_t *h;
+  float *u_out;
+  uint64_t *uex;
+};
+constexpr int kGemvJobs = 8;
+struct GemvJobs {
+  const uint8_t *codes[kGemvJobs];
+  const uint8_t *qscale[kGemvJobs];
+  const float *smax[kGemvJobs];
+  const uint16_t *x[kGemvJobs];
+  const uint16_t *A[kGemvJobs];
+  const uint16_t *B[kGemvJobs];
+  uint16_t *h[kGemvJobs];
+  float *u_out[kGemvJobs];
+  uint64_t *uex[kGemvJobs];
+  float scale[kGemvJobs];
+  int d_out[kGemvJobs], d_in[kGemvJobs], T[kGemvJobs], r[kGemvJobs], r_pad[kGemvJobs], sshift[kGemvJobs];
+  int wg0[kGemvJobs + 1];
+  int n;
+};
+hipError_t launch_gemv_fwd_many(const GemvJob *jobs, int n, uint32_t *sync, hipStream_t st);
 
 // gemm.hip: T > 16 (and any T the weight-streaming kernel does not take).
 // Work split of one contraction over 256 x 256 output tiles (gm x gn of them,

@@ -66,6 +66,17 @@ _lib.qlora_adamw_step_host.argtypes = [ctypes.c_void_p, _i64, _i64, _vp, _vp, _v
 _lib.qlora_adamw_step_host.restype = ctypes.c_int
 _lib.qlora_forward.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.qlora_forward.restype = ctypes.c_int
+
+
+class _ForwardJob(ctypes.Structure):
+    _fields_ = [("W", _W), ("x", _vp), ("T", _i64), ("A", _vp), ("B", _vp), ("r", _i32), ("alpha", _f32),
+                ("h", _vp), ("u_out", _vp)]
+
+
+_lib.qlora_forward_many.argtypes = [ctypes.POINTER(_ForwardJob), _i32, _vp, _sz, _vp]
+_lib.qlora_forward_many.restype = ctypes.c_int
+_lib.qlora_forward_many_workspace_bytes.argtypes = [_i32]
+_lib.qlora_forward_many_workspace_bytes.restype = _sz
 _lib.qlora_forward_noalloc.argtypes = [_W, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp]
 _lib.qlora_forward_noalloc.restype = ctypes.c_int
 _lib.qlora_workspace_fallbacks.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
@@ -443,6 +454,51 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
     _check(_lib.qlora_forward(ctypes.byref(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u),
                               _ptr(ws), ws.numel(), _stream(x.device)), "qlora_forward")
     return h, u
+
+
+MAX_FORWARD_JOBS = 64  # QLORA_MAX_FORWARD_JOBS
+
+
+def qlora_forward_many_workspace_bytes(count: int) -> int:
+    return int(_lib.qlora_forward_many_workspace_bytes(int(count)))
+
+
+def qlora_forward_many(jobs, ws: torch.Tensor | None = None):
+    """Several independent forwards of T <= 16 tokens in as few launches as possible (qlora_forward_many).
+
+    jobs: a sequence of dicts with keys w, x, A, B, alpha and optionally h, u (preallocated outputs) and save_u,
+    as for qlora_forward. Returns [(h, u), ...] in job order. No job's output may overlap another job's input
+    or output.
+    """
+    jobs = list(jobs)
+    if not 1 <= len(jobs) <= MAX_FORWARD_JOBS:
+        raise ValueError(f"between 1 and {MAX_FORWARD_JOBS} jobs, got {len(jobs)}")
+    args, outs = [], []
+    dev = None
+    for i, j in enumerate(jobs):
+        w = j["w"]
+        T, r, h, u = _forward_args(w, j["x"], j.get("A"), j.get("B"), j.get("h"), j.get("u"), j.get("save_u", False))
+        if T > 16:
+            raise ValueError(f"job {i}: T = {T}; the grouped forward takes T <= 16")
+        if dev is None:
+            dev = w.codes.device
+        elif w.codes.device != dev:
+            raise ValueError(f"job {i} is on {w.codes.device}, job 0 on {dev}")
+        args.append((w, j["x"], T, j.get("A"), j.get("B"), r, float(j["alpha"]), h, u))
+        outs.append((h, u))
+    nbytes = qlora_forward_many_workspace_bytes(len(jobs))
+    if ws is None:
+        ws = workspace(dev, nbytes)
+    else:
+        _own_workspace(ws, nbytes)
+        _check_devices(dev, ws=ws)
+    cws = [a[0]._c() for a in args]  # kept alive for the call
+    arr = (_ForwardJob * len(args))()
+    for k, (a, cw) in enumerate(zip(args, cws)):
+        w, x, T, A, B, r, alpha, h, u = a
+        arr[k] = _ForwardJob(ctypes.pointer(cw), _ptr(x), T, _ptr(A), _ptr(B), r, alpha, _ptr(h), _ptr(u))
+    _check(_lib.qlora_forward_many(arr, len(args), _ptr(ws), ws.numel(), _stream(dev)), "qlora_forward_many")
+    return outs
 
 
 def qlora_forward_noalloc(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,

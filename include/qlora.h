@@ -179,6 +179,44 @@ int qlora_forward(const qlora_nf4_weight *W, const uint16_t *x, int64_t T, const
                   size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Several independent forwards of T <= 16 tokens each (the weight-streaming
+ * regime) in as few launches as possible: per job, the qlora_forward of
+ * "QLoRA의 수식" with that job's weight, input, adapter and outputs. Jobs that
+ * share a kernel variant (x of at most 136 KB or not; d_in/64 a multiple of 4 or
+ * not) run in one launch, up to 8 of them, and pay its start and its tail once;
+ * the compute units are shared out by weight bytes. For projections that
+ * cannot be stacked into one weight: separate q, k, v or gate, up weights with
+ * their own adapters, or the same step's calls of several models or adapters.
+ *   jobs   host array of `count` (1 <= count <= QLORA_MAX_FORWARD_JOBS) job
+ *          structs; each job's fields are qlora_forward's arguments, with T <= 16
+ *   ws     device workspace of at least qlora_forward_many_workspace_bytes(count)
+ *          bytes, its counter region zero as for qlora_forward
+ * The jobs must be independent: no job's output may overlap another job's input
+ * or output. u_out is bit-identical to qlora_forward's; h differs from it at
+ * most in the float32 summation order of the K segments (a job's share of the
+ * compute units decides which wave sums which segments), and is the same bits
+ * on every call with the same jobs. Every job is checked before anything is
+ * launched (an argument error writes nothing). Errors: those of qlora_forward;
+ * SHAPE for a job with T > 16 or a count outside 1..QLORA_MAX_FORWARD_JOBS.
+ */
+typedef struct {
+  const qlora_nf4_weight *W;
+  const uint16_t *x;   /* device bf16 [T, d_in] */
+  int64_t T;           /* 1..16 */
+  const uint16_t *A;   /* device bf16 [r, d_in] or NULL */
+  const uint16_t *B;   /* device bf16 [d_out, r] or NULL */
+  int32_t r;
+  float alpha;
+  uint16_t *h;         /* device bf16 [T, d_out], overwritten */
+  float *u_out;        /* device f32 [T, r] or NULL */
+} qlora_forward_job;
+#define QLORA_MAX_FORWARD_JOBS 64
+int qlora_forward_many(const qlora_forward_job *jobs, int32_t count, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+/* Workspace bytes of qlora_forward_many for `count` jobs (0 for a count outside 1..QLORA_MAX_FORWARD_JOBS). */
+size_t qlora_forward_many_workspace_bytes(int32_t count);
+
+/*
  * Backward through the frozen restored weight ("QLoRA의 수식", "명제 1"):
  *   v  = dY B
  *   dX = dY W_hat + (alpha/r) v A        device bf16 [T, d_in], nullable

@@ -146,6 +146,42 @@ def test_quantize_many_rejects_bad_arguments_before_launching():
     assert q.lib.qlora_quantize_many(nul, 0, ws, 2, None, None) == ERR_NULL
 
 
+def _job(w, x=GOOD, T=4, A=GOOD, B=GOOD, r=8, h=GOOD, u=None):
+    return q._ForwardJob(ctypes.pointer(w), x, T, A, B, r, 16.0, h, u)
+
+
+def test_forward_many_rejects_bad_arguments_before_launching():
+    """Every job is checked before any launch (here no GPU is there to launch on); the workspace covers the
+    counter region and one rank-256 exchange buffer per job."""
+    ws1 = q.qlora_forward_many_workspace_bytes(1)
+    assert ws1 == 65536 + 4 * 16 * 256 * 8
+    assert q.qlora_forward_many_workspace_bytes(3) == 65536 + 3 * 4 * 16 * 256 * 8
+    assert q.qlora_forward_many_workspace_bytes(0) == 0
+    assert q.qlora_forward_many_workspace_bytes(q.MAX_FORWARD_JOBS + 1) == 0
+    ws_need = q.qlora_forward_many_workspace_bytes(3)
+    wts = [_w(), _w(), _w()]
+
+    def call(jobs, count=None, ws=GOOD, ws_bytes=ws_need):
+        arr = (q._ForwardJob * len(jobs))(*jobs)
+        return q.lib.qlora_forward_many(arr, len(jobs) if count is None else count, ws, ws_bytes, None)
+
+    good = [_job(w) for w in wts]
+    assert call(good, count=0) == ERR_SHAPE
+    assert call(good, count=q.MAX_FORWARD_JOBS + 1) == ERR_SHAPE
+    assert q.lib.qlora_forward_many(None, 1, GOOD, ws_need, None) == ERR_NULL
+    assert call(good[:2] + [_job(wts[2], T=17)]) == ERR_SHAPE          # the third job: T > 16
+    assert call(good[:2] + [_job(_w(d_in=100))]) == ERR_SHAPE         # d_in % 64
+    assert call([good[0], _job(wts[1], r=12), good[2]]) == ERR_SHAPE   # r % 8
+    assert call([good[0], _job(wts[1], x=None), good[2]]) == ERR_NULL
+    assert call([good[0], _job(wts[1], h=None), good[2]]) == ERR_NULL
+    assert call([good[0], _job(wts[1], A=None), good[2]]) == ERR_NULL  # r > 0 with only B
+    assert call([good[0], _job(wts[1], x=BAD), good[2]]) == ERR_ALIGN
+    assert call([good[0], good[1], _job(wts[2], u=BAD)]) == ERR_ALIGN
+    assert call(good, ws_bytes=ws_need - 1) == ERR_WORKSPACE
+    assert call(good, ws=None) == ERR_NULL
+    assert call(good, ws=BAD) == ERR_ALIGN
+
+
 def test_merge_rejects_bad_arguments():
     w = _w()
     assert q.lib.qlora_merge(ctypes.byref(w), GOOD, GOOD, 8, 16.0, None, None) == ERR_NULL
