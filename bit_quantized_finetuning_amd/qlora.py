@@ -459,6 +459,30 @@ def qlora_forward(w: NF4Weight, x: torch.Tensor, A: torch.Tensor | None, B: torc
 MAX_FORWARD_JOBS = 64  # QLORA_MAX_FORWARD_JOBS
 
 
+def _span(t):
+    return None if t is None or t.numel() == 0 else (t.data_ptr(), t.data_ptr() + t.numel() * t.element_size())
+
+
+def _check_independent(args):
+    """The jobs of one grouped launch run at the same time: no output may overlap an input or output of any job
+    (its own inputs included)."""
+    spans = []
+    for i, (w, x, T, A, B, r, alpha, h, u) in enumerate(args):
+        for name, t in (("x", x), ("A", A), ("B", B), ("codes", w.codes), ("qscale", w.qscale), ("smax", w.smax)):
+            spans.append((i, name, False, _span(t)))
+        for name, t in (("h", h), ("u", u)):
+            spans.append((i, name, True, _span(t)))
+    for i, n1, out1, s1 in spans:
+        if not out1 or s1 is None:
+            continue
+        for k, n2, out2, s2 in spans:
+            if s2 is None or (k == i and n2 == n1):
+                continue
+            if s1[0] < s2[1] and s2[0] < s1[1]:
+                raise ValueError(f"job {i}'s {n1} overlaps job {k}'s {n2}: the jobs of a grouped call must be "
+                                 "independent")
+
+
 def qlora_forward_many_workspace_bytes(count: int) -> int:
     return int(_lib.qlora_forward_many_workspace_bytes(int(count)))
 
@@ -486,6 +510,7 @@ def qlora_forward_many(jobs, ws: torch.Tensor | None = None):
             raise ValueError(f"job {i} is on {w.codes.device}, job 0 on {dev}")
         args.append((w, j["x"], T, j.get("A"), j.get("B"), r, float(j["alpha"]), h, u))
         outs.append((h, u))
+    _check_independent(args)
     nbytes = qlora_forward_many_workspace_bytes(len(jobs))
     if ws is None:
         ws = workspace(dev, nbytes)

@@ -123,3 +123,21 @@ def test_dtype_casts_leave_storage_and_adapters_alone():
     m2.smax.fill_(0.5)
     m2.load_state_dict(sd)
     assert torch.equal(m2.w.smax, s0)
+
+
+def test_grouped_forward_checks(w):
+    x, A, B = bf(T, D_IN), bf(R, D_IN), bf(D_OUT, R)
+    _raises(ValueError, "between 1 and", q.qlora_forward_many, [])
+    _raises(ValueError, "between 1 and", q.qlora_forward_many, [{}] * (q.MAX_FORWARD_JOBS + 1))
+    # the jobs of one launch run at the same time: outputs may not overlap any job's inputs or outputs
+    x1 = bf(T, D_IN)
+    ok = [(w, x, T, A, B, R, 16.0, bf(T, D_OUT), f32(T, R)), (w, x1, T, A, B, R, 16.0, bf(T, D_OUT), None)]
+    q._check_independent(ok)  # a weight and adapters shared between jobs are inputs only
+    over_x = x1.view(-1)[:T * D_OUT].view(T, D_OUT)  # job 0's h inside job 1's x
+    _raises(ValueError, "overlaps job 1's x", q._check_independent,
+            [(w, x, T, A, B, R, 16.0, over_x, None), (w, x1, T, A, B, R, 16.0, bf(T, D_OUT), None)])
+    hh = bf(2 * T, D_OUT)
+    _raises(ValueError, "overlaps job 1's h", q._check_independent,
+            [(w, x, T, A, B, R, 16.0, hh[:T], None), (w, x1, T, A, B, R, 16.0, hh[T - 1:2 * T - 1], None)])
+    own = x.view(-1)[:T * D_OUT].view(T, D_OUT)  # a job's h over its own x
+    _raises(ValueError, "overlaps job 0's x", q._check_independent, [(w, x, T, A, B, R, 16.0, own, None)])
