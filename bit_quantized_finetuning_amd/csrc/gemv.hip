@@ -191,15 +191,15 @@ static hipError_t launch_group(const GemvJob *const *g, int n, uint32_t *sync, b
   GemvJobs J{};
   J.n = n;
   int64_t wsum = 0, grid = 0;
-  int64_t G[kGemvJobs], W[kGemvJobs], RT[kGemvJobs];
+  int64_t G[kGemvJobs], W[kGemvJobs], RT[kGemvJobs], lo[kGemvJobs];
   for (int i = 0; i < n; ++i) {
     RT[i] = (g[i]->d_out + 15) / 16;
     W[i] = RT[i] * (g[i]->d_in / kBlock);
     wsum += W[i];
   }
   for (int i = 0; i < n; ++i) {
-    const int64_t lo = std::max<int64_t>(gemv_producers(*g[i]), 1);
-    G[i] = std::max(lo, std::min(RT[i], cus * W[i] / wsum));
+    lo[i] = std::max<int64_t>(gemv_producers(*g[i]), 1);
+    G[i] = std::max(lo[i], std::min(RT[i], cus * W[i] / wsum));
     grid += G[i];
   }
   // compute units left over go one at a time to the job with the most weight per workgroup
@@ -210,6 +210,16 @@ static hipError_t launch_group(const GemvJob *const *g, int n, uint32_t *sync, b
     if (best < 0) break;
     ++G[best];
     ++grid;
+  }
+  // the producers' minimums can push the total past one residency (the launcher keeps them to half of it):
+  // take workgroups back from the jobs with the least weight per workgroup
+  while (grid > cus) {
+    int best = -1;
+    for (int i = 0; i < n; ++i)
+      if (G[i] > lo[i] && (best < 0 || W[i] * G[best] < W[best] * G[i])) best = i;
+    if (best < 0) break;
+    --G[best];
+    --grid;
   }
   size_t lds = 0;
   int64_t wg = 0;
