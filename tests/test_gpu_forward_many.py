@@ -45,6 +45,9 @@ MIXED = [
 ]
 # eleven jobs of one kernel variant: two launches
 ELEVEN = [(256 + 64 * i, 512, 8 * (i % 4), 1 + i % 16, "dq") for i in range(11)]
+# a rank-256 job needs 64 producer workgroups although it has 33 row tiles; with a large job beside it the
+# shares first add up to more than the compute units and are taken back from the large job
+TRIM = [(528, 1344, 256, 4, "dq"), (4096, 1344, 0, 4, "dq")]
 
 
 def _cases(spec, cfg):
@@ -72,7 +75,7 @@ def _same(a, b):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
-@pytest.mark.parametrize("spec,cfg", [(MIXED, 140), (ELEVEN, 141)], ids=["mixed", "eleven"])
+@pytest.mark.parametrize("spec,cfg", [(MIXED, 140), (ELEVEN, 141), (TRIM, 144)], ids=["mixed", "eleven", "trim"])
 def test_forward_many_parity(spec, cfg):
     say(f"forward_many {len(spec)} jobs")
     cases = _cases(spec, cfg)
