@@ -650,7 +650,9 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
                 "kernel": "whole forward + backward step (all kernels)"}
 
     per_call = per_call_times(torch, dev, calls, run_call, chunk) if not (args.no_graph or args.no_per_call) else []
-    grouped = (grouped_times(torch, dev, q, calls, nT, chunk, args.steps, fb, wbytes_step)
+    grouped = (grouped_times(torch, dev, q, calls, nT, chunk, args.steps, fb, wbytes_step,
+                             recorded_traffic(key="grouped_traffic_bytes_per_launch")
+                             if wname == "llama7b_skinny" and not ABSMAX_STORAGE[0] else None)
                if not (bw or args.no_graph) else None)
 
     if args.copy_calibration:
@@ -701,7 +703,7 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_k_gemv_fwd_llama7b_skin
 FWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_qlora_forward_65b_layer.json")
 
 
-def recorded_traffic(record=TRAFFIC_RECORD):
+def recorded_traffic(record=TRAFFIC_RECORD, key="traffic_bytes_per_launch"):
     """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counter runs (the record names the command and
     the sources it was taken on), or None when the record is missing or those sources changed since."""
     import hashlib
@@ -713,12 +715,12 @@ def recorded_traffic(record=TRAFFIC_RECORD):
                 h.update(fh.read())
         if h.hexdigest() != rec["sources_sha256"]:
             return None
-        return int(rec["traffic_bytes_per_launch"])
+        return int(rec[key])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def grouped_times(torch, dev, q, calls, nT, chunk, steps, fb_step, wbytes_step):
+def grouped_times(torch, dev, q, calls, nT, chunk, steps, fb_step, wbytes_step, traffic=None):
     """The same step with its calls, which are independent, given to qlora_forward_many: one launch per step
     when they share a kernel variant. Graph-timed like the step, on the same rotating weight copies and inputs."""
     ws = torch.zeros(q.qlora_forward_many_workspace_bytes(len(calls)), dtype=torch.uint8, device=dev)
@@ -734,7 +736,7 @@ def grouped_times(torch, dev, q, calls, nT, chunk, steps, fb_step, wbytes_step):
     achieved = fb_step / (ms * 1e-3) / 1e9
     return {"ms_per_step": round(ms, 5), "steps": n, "weight_GBs": round(wbytes_step / (ms * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "kernel": ("k_gemv_fwd_many (qlora_forward_many: one launch per kernel variant among "
                                     "the step's calls)"),
                          "bytes_per_step": round(fb_step), "us_per_step": round(ms * 1e3, 3)},
