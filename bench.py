@@ -35,6 +35,8 @@ Other workloads (--workload) are records, not the headline line:
       r=8 on q and v);
   14b_stack_fused  the same layer with q/k/v and gate/up each stacked into one call that reads its input once
       (q and v adapters as one block-diagonal rank-16 pair);
+  65b_layer_fused  the 65B layer with q/k/v (three rank-64 adapters as one block-diagonal rank-192 pair) and
+      gate/up stacked, TFLOP/s counted with the unstacked projections' algorithmic flops;
   14b_quantize  one pass quantizing all 280 bf16 weights of the 14B-style stack (13.2 G parameters, generated
       on the device from a seeded generator) with qlora_quantize_many (32 weights per launch), and beside it the
       same pass as one qlora_quantize call per weight;
@@ -62,7 +64,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-dequant GEMM+LoRA TFLOP/s and weight GB/s, % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-WORKLOAD_CHOICES = ["llama7b_skinny", "65b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused",
+WORKLOAD_CHOICES = ["llama7b_skinny", "65b_skinny", "linear1024", "13b_4096tok", "65b_layer", "14b_stack", "14b_stack_fused", "65b_layer_fused",
                     "14b_chain", "14b_quantize",
                     "merge_llama7b", "13b_paged_adamw"]
 
@@ -128,7 +130,17 @@ def bwd_flops(d_out, d_in, r, T):
     return 2 * T * d_in * d_out + 4 * T * r * (d_in + d_out)
 
 
-TRAIN_WORKLOADS = ("65b_layer", "13b_4096tok", "14b_stack", "14b_stack_fused", "linear1024")
+def proj_flops(p, T, backward):
+    """Algorithmic flops of one call. A stacked call counts each adapter on its own projection's rows, not the
+    zeros of its block-diagonal B: the same count as the projections called one by one."""
+    f = bwd_flops if backward else fwd_flops
+    if not p.b_rows:
+        return f(p.d_out, p.d_in, p.r, T)
+    rk = p.r // len(p.b_rows)
+    return f(p.d_out, p.d_in, 0, T) + sum(f(r1 - r0, p.d_in, rk, T) - f(r1 - r0, p.d_in, 0, T) for r0, r1 in p.b_rows)
+
+
+TRAIN_WORKLOADS = ("65b_layer", "65b_layer_fused", "13b_4096tok", "14b_stack", "14b_stack_fused", "linear1024")
 
 
 def main():
@@ -162,7 +174,7 @@ def main():
     return bench_graph(args, torch, q, synth, dev, args.workload)
 
 
-def bench_train(args, torch, q, synth, dev, wname):
+def bench_train(args, torch, q, synth, dev, wname, emit=True):
     """Forward + backward of every projection of a workload, eager launches, HIP events around every call."""
     wl = synth.WORKLOADS[wname]
     cfg = synth.WORKLOAD_SEED[wname]
@@ -232,8 +244,8 @@ def bench_train(args, torch, q, synth, dev, wname):
     fwd_ms = [np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs]) for i in range(n)]
     bwd_ms = [np.mean([e[2 * n + 2 * i].elapsed_time(e[2 * n + 2 * i + 1]) for e in evs]) for i in range(n)]
 
-    ff = sum(fwd_flops(p.d_out, p.d_in, p.r, T) for p, *_ in projs)
-    bf = sum(bwd_flops(p.d_out, p.d_in, p.r, T) for p, *_ in projs)
+    ff = sum(proj_flops(p, T, False) for p, *_ in projs)
+    bf = sum(proj_flops(p, T, True) for p, *_ in projs)
     tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
     # the fused dequant-GEMM + LoRA forward: algorithmic flops of all forward calls over their summed duration
     fwd_tf = ff / (sum(fwd_ms) * 1e-3) / 1e12
@@ -245,10 +257,11 @@ def bench_train(args, torch, q, synth, dev, wname):
                       "adapter term as extra K columns)" % T if T >= 65 else "qlora_forward",
             "flops_per_launch": round(ff / n), "us_per_launch": round(1e3 * sum(fwd_ms) / n, 2),
             "launches": args.steps * n, "timing": "HIP events around every forward call in the timed region"}
+    label_traffic(roof, FWD_TRAFFIC_RECORD)
     per_call = []
     for i, (p, *_r) in enumerate(projs):
-        for kind, ms, fl in (("fwd", fwd_ms[i], fwd_flops(p.d_out, p.d_in, p.r, T)),
-                             ("bwd", bwd_ms[i], bwd_flops(p.d_out, p.d_in, p.r, T))):
+        for kind, ms, fl in (("fwd", fwd_ms[i], proj_flops(p, T, False)),
+                             ("bwd", bwd_ms[i], proj_flops(p, T, True))):
             per_call.append({"proj": f"{p.name} {p.d_out}x{p.d_in}", "call": kind, "r": p.r,
                              "us": round(ms * 1e3, 1), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1)})
     wbytes = 2 * sum(weight_bytes(p.d_out, p.d_in) for p, *_ in projs)
@@ -280,6 +293,8 @@ def bench_train(args, torch, q, synth, dev, wname):
     print(f"[bench] {wname}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if args.copy_calibration:
         copy_calibration(torch, dev)
+    if not emit:
+        return line
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_train(args, wl, cfg, ms_step, ff + bf)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
@@ -643,6 +658,7 @@ def bench_graph(args, torch, q, synth, dev, wname, paged=False, emit=True):
                 "kernel": "k_gemv_fwd (qlora_forward, T <= 16)",
                 "bytes_per_launch": round(fb / len(calls)), "us_per_launch": round(us_launch, 3),
                 "launches": launches}
+        label_traffic(roof)
     else:
         achieved = (ff + bf) / (ms_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -703,6 +719,15 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_k_gemv_fwd_llama7b_skin
 FWD_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_qlora_forward_65b_layer.json")
 
 
+def label_traffic(roof, record=TRAFFIC_RECORD):
+    """A traffic figure in a roofline object is a recorded one: say so, and from where."""
+    if roof.get("traffic") is not None:
+        roof["traffic_source"] = ("recorded, not measured in this run: %s (FETCH_SIZE and WRITE_SIZE counter runs, "
+                                  "scaled by a copy calibration; the sources it was taken on are hash-checked)"
+                                  % os.path.relpath(record, ROOT))
+    return roof
+
+
 def recorded_traffic(record=TRAFFIC_RECORD, key="traffic_bytes_per_launch"):
     """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counter runs (the record names the command and
     the sources it was taken on), or None when the record is missing or those sources changed since."""
@@ -735,11 +760,11 @@ def grouped_times(torch, dev, q, calls, nT, chunk, steps, fb_step, wbytes_step, 
     ms, n = _timed_graph(torch, dev, body, steps, chunk)
     achieved = fb_step / (ms * 1e-3) / 1e9
     return {"ms_per_step": round(ms, 5), "steps": n, "weight_GBs": round(wbytes_step / (ms * 1e-3) / 1e9, 1),
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "roofline": label_traffic({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "kernel": ("k_gemv_fwd_many (qlora_forward_many: one launch per kernel variant among "
                                     "the step's calls)"),
-                         "bytes_per_step": round(fb_step), "us_per_step": round(ms * 1e3, 3)},
+                         "bytes_per_step": round(fb_step), "us_per_step": round(ms * 1e3, 3)}),
             "fallbacks": q.qlora_workspace_fallbacks(ws)}
 
 

@@ -68,6 +68,16 @@ WORKLOADS = {
                     Projection("gate_proj", 22016, 8192, 64, 16.0),
                     Projection("up_proj", 22016, 8192, 64, 16.0),
                     Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
+    # The same 65B layer as the layer driver runs it: the projections of one input stacked into one call each,
+    # q/k/v (24576 x 8192, three rank-64 adapters as a block-diagonal rank-192 pair, alpha tripled so the scale
+    # stays 16/64) and gate/up (44032 x 8192, two rank-64 adapters). The quantized storage of a stacked weight
+    # is that of its parts laid end to end (every part holds a whole number of 256-block groups).
+    "65b_layer_fused": Workload("65b_layer_fused", "65B decoder layer, hidden 8192, MLP 22016, LoRA r=64 alpha=16 "
+                   "on all projections, 4096 tokens, fwd+bwd, q/k/v and gate/up each as one stacked call",
+                   (Projection("qkv_proj", 24576, 8192, 192, 48.0, b_rows=((0, 8192), (8192, 16384), (16384, 24576))),
+                    Projection("o_proj", 8192, 8192, 64, 16.0),
+                    Projection("gate_up_proj", 44032, 8192, 128, 32.0, b_rows=((0, 22016), (22016, 44032))),
+                    Projection("down_proj", 8192, 22016, 64, 16.0)), (4096,), True, "f32"),
     # The weight-streaming regime on the 65B layer's larger weights (34-93 MB per call instead of 9-23 MB):
     # how close the T <= 16 kernel gets to HBM once the stream is long against its fixed latency.
     "65b_skinny": Workload("65b_skinny", "65B decoder-layer projections 8192x8192, 22016x8192 and 8192x22016, "
@@ -96,7 +106,7 @@ WORKLOADS = {
 }
 # second component of every RNG seed list, one per workload
 WORKLOAD_SEED = {"linear1024": 1, "llama7b_skinny": 2, "13b_4096tok": 3, "65b_layer": 4, "14b_stack": 5,
-                 "14b_stack_fused": 6, "65b_skinny": 7}
+                 "14b_stack_fused": 6, "65b_skinny": 7, "65b_layer_fused": 8}
 
 
 def rng(config: int, projection: int, tensor: int, seed: int = 0) -> np.random.Generator:
