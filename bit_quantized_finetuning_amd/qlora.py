@@ -418,6 +418,19 @@ def qlora_adamw_step_host(step: int, grad: torch.Tensor, master: torch.Tensor, m
                                       _ptr(param), int(threads)), "qlora_adamw_step_host")
 
 
+def _check_no_overlap(inputs: dict, outputs: dict):
+    """The kernels read their inputs while they write their outputs and workspace: no output may overlap an
+    input or another output (in-place calls are not supported)."""
+    named = [(n, _span(t), False) for n, t in inputs.items()] + [(n, _span(t), True) for n, t in outputs.items()]
+    for i, (n1, s1, out1) in enumerate(named):
+        if not out1 or s1 is None:
+            continue
+        for k, (n2, s2, _) in enumerate(named):
+            if k != i and s2 is not None and s1[0] < s2[1] and s2[0] < s1[1]:
+                raise ValueError(f"{n1} overlaps {n2}: outputs and workspace must not share memory with any "
+                                 "other argument")
+
+
 def _forward_args(w, x, A, B, h, u, save_u, ws=None):
     _check_weight(w)
     if not torch.is_tensor(x) or x.dim() != 2:
@@ -431,6 +444,8 @@ def _forward_args(w, x, A, B, h, u, save_u, ws=None):
     _arg(u, "u", torch.float32, (T, r))
     if ws is not None:
         _own_workspace(ws, qlora_workspace_bytes(w.d_out, w.d_in, T, r))
+    _check_no_overlap({"x": x, "A": A, "B": B, "codes": w.codes, "qscale": w.qscale, "smax": w.smax},
+                      {"h": h, "u": u, "ws": ws})
     dev = w.codes.device
     _check_devices(dev, qscale=w.qscale, smax=w.smax, x=x, A=A, B=B, h=h, u=u, ws=ws)
     if h is None:
@@ -587,6 +602,8 @@ def qlora_backward(w: NF4Weight, x: torch.Tensor | None, dY: torch.Tensor, A: to
     nbytes = qlora_workspace_bytes(w.d_out, w.d_in, T, r)
     if ws is not None:
         _own_workspace(ws, nbytes)
+    _check_no_overlap({"x": x, "dY": dY, "A": A, "B": B, "u_saved": u_saved, "codes": w.codes, "qscale": w.qscale,
+                       "smax": w.smax}, {"dX": dX, "dA": dA, "dB": dB, "ws": ws})
     dev = w.codes.device
     _check_devices(dev, qscale=w.qscale, smax=w.smax, x=x, dY=dY, A=A, B=B, u_saved=u_saved, dX=dX, dA=dA, dB=dB,
                    ws=ws)

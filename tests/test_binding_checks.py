@@ -60,6 +60,27 @@ def test_forward_checks(w):
     _raises(ValueError, "must be on a GPU", q.qlora_forward, w, x, None, None, 16.0)
 
 
+def test_outputs_must_not_alias_inputs(w):
+    A, B = bf(R, D_IN), bf(D_OUT, R)
+    buf = bf(T * (D_IN + D_OUT))
+    x, dY = buf[: T * D_IN].view(T, D_IN), buf[T * D_IN:].view(T, D_OUT)
+    _raises(ValueError, "h overlaps x", q.qlora_forward, w, x, A, B, 16.0,
+            h=buf[T * 64:T * (64 + D_OUT)].view(T, D_OUT))
+    _raises(ValueError, "h overlaps x", q.qlora_forward_noalloc, w, x, A, B, 16.0, h=buf[:T * D_OUT].view(T, D_OUT))
+    hb = bf(T * D_OUT + 8)
+    _raises(ValueError, "h overlaps u|u overlaps h", q.qlora_forward, w, x, A, B, 16.0,
+            h=hb[:T * D_OUT].view(T, D_OUT), u=hb.view(torch.float32)[:T * R].view(T, R))
+    _raises(ValueError, "dX overlaps dY", q.qlora_backward, w, bf(T, D_IN), dY, A, B, 16.0,
+            dX=buf[T * D_OUT:].view(T, D_IN))
+    uf = f32(T * R + D_OUT * R)
+    _raises(ValueError, "dB overlaps u_saved", q.qlora_backward, w, bf(T, D_IN), bf(T, D_OUT), A, B, 16.0,
+            u_saved=uf[:T * R].view(T, R), dB=uf[T * R - 8:T * R - 8 + D_OUT * R].view(D_OUT, R))
+    # disjoint views of one buffer are fine: the device rule is what stops a CPU call
+    _raises(ValueError, "must be on a GPU", q.qlora_forward, w, x, A, B, 16.0, h=dY)
+    _raises(ValueError, "must be on a GPU", q.qlora_backward, w, x, dY, A, B, 16.0, u_saved=uf[:T * R].view(T, R),
+            dB=uf[T * R:].view(D_OUT, R))
+
+
 def test_backward_checks(w):
     x, dY, A, B = bf(T, D_IN), bf(T, D_OUT), bf(R, D_IN), bf(D_OUT, R)
     _raises(ValueError, "dY must have shape", q.qlora_backward, w, x, bf(T, D_OUT + 16), A, B, 16.0)
