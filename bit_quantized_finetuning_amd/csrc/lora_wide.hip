@@ -128,15 +128,16 @@ __global__ __launch_bounds__(256) void k_lora_tall(const uint16_t *__restrict__ 
                           : u32x4{0u, 0u, 0u, 0u};  // (wave-uniform) no such tile
       }
     }
+    // Unconditional MFMAs: a wave past the last column tile multiplies its
+    // zero B fragment, so that accumulator stays zero and is never stored. (A
+    // branch around them would make the compiler copy the accumulators out of
+    // and back into the matrix registers around every group of four.)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < kNtw; ++j) {
-        if (wave + 4 * j < nt) {  // wave-uniform
+      for (int j = 0; j < kNtw; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(a[h][i], b[h][j], acc[i][j]);
-        }
-      }
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(a[h][i], b[h][j], acc[i][j]);
   }
 
   // lane (li, g): tokens 16i + 4g + e of token tile i, column 16 ct + li
